@@ -1,0 +1,483 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, not against the oracle itself.
+
+Sources (cited by title and section):
+  [README]   VisionHOPE README: "SRNL and VisionHOPE operator", "Fast inference".
+  [OVERVIEW] "VisionHOPE Model Overview: Architecture, Benchmarks, and
+             Practical Limits": "Four-Directional Scanning and Spatial
+             Chunking", "Why the Stability Controls Matter".
+  [SUMMARY]  "VisionHOPE: Visual Backbones as Self-Modifying Learning
+             Systems": write-rule, stabilisation, 2-D map and ablation
+             paragraphs.
+
+Pins used:
+  * route orders and chunk partitions written out from the definitions
+    (tests/golden/*.json);
+  * symmetries: reverse route == forward route on the grid flipped in both
+    axes; column route == row route on the transposed grid (bitwise);
+  * an independent dense brute force in extended precision (numpy
+    longdouble): per token it builds the retained transition
+    R = alpha I - eta'' k^ k^T and the L2 gradient G = (B k^ - B v) k^T as
+    matrices and applies M <- M R - eta'' G; G is itself checked against
+    central finite differences of 1/2 |M k^ - B v|^2;
+  * chunk = 1 equals a separately written token-wise recurrence;
+  * closed form at x = 0: y_t = (alpha_max/2)^(t+1) M_c q_t;
+  * linearity of y in q and in the initial content memory;
+  * the non-expansion guarantees the pages state (per token, relative to the
+    chunk boundary) on random and adversarial inputs, and a negative
+    control showing the check has teeth without the soft cap;
+  * the kernels' "Q-form" rewrite (M = B Q, Q_0 = I per chunk) equals the
+    five-memory form;
+  * fusion equals an independent restore (argsort of the route order) and
+    per-channel weighted sum.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from self_referential_memory_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _route_order(r, H, W):
+    """Flat grid indices in route r's visiting order, from numpy reshapes."""
+    grid = np.arange(H * W).reshape(H, W)
+    row = grid.reshape(-1)
+    col = grid.T.reshape(-1)
+    return {0: row, 1: row[::-1], 2: col, 3: col[::-1]}[r]
+
+
+# ---------------------------------------------------------------- routes
+
+def test_route_orders_golden():
+    g = json.load(open(os.path.join(GOLDEN, "routes_2x3.json")))
+    H, W = g["H"], g["W"]
+    for r, cells in g["routes"].items():
+        got = [list(oracle.route_index(int(r), H, W, t)) for t in range(H * W)]
+        assert got == cells, r
+
+
+@pytest.mark.parametrize("H,W", [(1, 1), (1, 7), (7, 1), (3, 5), (14, 20), (56, 56)])
+def test_route_bijection(H, W):
+    for r in range(4):
+        seen = set()
+        for t in range(H * W):
+            i, j = oracle.route_index(r, H, W, t)
+            assert 0 <= i < H and 0 <= j < W
+            seen.add((i, j))
+        assert len(seen) == H * W
+        exp = _route_order(r, H, W)
+        got = [oracle.route_index(r, H, W, t) for t in range(H * W)]
+        assert [i * W + j for i, j in got] == list(exp)
+
+
+def test_chunking_golden():
+    g = json.load(open(os.path.join(GOLDEN, "chunking.json")))
+    for case in g["cases"]:
+        H, W = case["H"], case["W"]
+        cr, cc = case["chunk_row"], case["chunk_col"]
+        assert oracle.chunk_len(0, H, W, cr, cc) == case["row_chunk_len"]
+        assert oracle.chunk_len(1, H, W, cr, cc) == case["row_chunk_len"]
+        assert oracle.chunk_len(2, H, W, cr, cc) == case["col_chunk_len"]
+        assert oracle.chunk_len(3, H, W, cr, cc) == case["col_chunk_len"]
+        if "heads" in case:
+            assert case["C"] % case["head_dim"] == 0
+            assert case["C"] // case["head_dim"] == case["heads"]
+        # the partition as the oracle runs it: token position inside its
+        # chunk restarts at 0 at each boundary (trace column 17)
+        d = 4
+        x = synth.normals(11, 1, H * W * d).reshape(1, H, W, d)
+        st = synth.states(11, 1, d, 0.1)
+        for key, r in (("row_chunks", 0), ("col_chunks", 2)):
+            if key not in case:
+                continue
+            _, tr = oracle.scan(x, st, 1, d, 1 << r, chunk_row=cr, chunk_col=cc,
+                                trace=True)
+            pos = tr[0, 0, 0, :, 17].astype(int)
+            starts = list(np.flatnonzero(pos == 0)) + [H * W]
+            sizes = [b - a for a, b in zip(starts[:-1], starts[1:])]
+            assert sizes == case[key]
+
+
+# ------------------------------------------------------------ symmetries
+
+def _wl(H, W, d=4, heads=2, seed=5, std=0.3, B=2):
+    C = heads * d
+    x = synth.normals(seed, 1, B * H * W * C).reshape(B, H, W, C)
+    st = synth.states(seed, heads, d, std).astype(np.float64)
+    return x, st
+
+
+def test_reverse_route_is_forward_on_flipped_grid():
+    x, st = _wl(5, 7)
+    for fwd, rev in ((0, 1), (2, 3)):
+        st2 = st.copy()
+        st2[fwd] = st[rev]          # the reverse route's own states
+        y_rev = oracle.scan(x, st, 2, 4, 1 << rev)
+        y_fwd = oracle.scan(np.ascontiguousarray(x[:, ::-1, ::-1]), st2, 2, 4, 1 << fwd)
+        assert np.array_equal(y_rev, y_fwd)
+
+
+def test_column_route_is_row_route_on_transposed_grid():
+    x, st = _wl(5, 7)
+    xt = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+    for col, row in ((2, 0), (3, 1)):
+        st2 = st.copy()
+        st2[row] = st[col]
+        y_col = oracle.scan(x, st, 2, 4, 1 << col)
+        y_row = oracle.scan(xt, st2, 2, 4, 1 << row)
+        assert np.array_equal(y_col, y_row)
+        # with overrides the chunk lengths swap too
+        y_col = oracle.scan(x, st, 2, 4, 1 << col, chunk_row=2, chunk_col=3)
+        y_row = oracle.scan(xt, st2, 2, 4, 1 << row, chunk_row=3, chunk_col=2)
+        assert np.array_equal(y_col, y_row)
+
+
+# ------------------------------------------------------------ brute force
+
+LD = np.longdouble
+
+
+def _sig(z):
+    return LD(1) / (LD(1) + np.exp(-z))
+
+
+def brute_force(x, st, heads, d, route_mask, q=None, alpha_max=0.9, eps=1e-6,
+                chunk_row=0, chunk_col=0, cap="soft", clamp=True):
+    """Dense extended-precision restatement: per token build R and G as
+    matrices and apply M <- M R - eta'' G to every memory (vectors as 1 x d)."""
+    B, H, W, C = x.shape
+    N = H * W
+    X = x.reshape(B, N, C).astype(LD)
+    Qx = (x if q is None else q).reshape(B, N, C).astype(LD)
+    am = LD(alpha_max)
+    I = np.eye(d, dtype=LD)
+    out = []
+    for r in range(4):
+        if not (route_mask >> r) & 1:
+            continue
+        L = (chunk_row or W) if r < 2 else (chunk_col or H)
+        order = _route_order(r, H, W)
+        y = np.zeros((B, N, C), dtype=LD)
+        for b in range(B):
+            for h in range(heads):
+                s = st[r, h].astype(LD)
+                dd = d * d
+                mems = [s[:dd].reshape(d, d), s[dd:2 * dd].reshape(d, d),
+                        s[2 * dd:3 * dd].reshape(d, d),
+                        s[3 * dd:3 * dd + d].reshape(1, d),
+                        s[3 * dd + d:].reshape(1, d)]
+                sl = slice(h * d, (h + 1) * d)
+                for c0 in range(0, N, L):
+                    Bs = [m.copy() for m in mems]
+                    for t in range(c0, min(c0 + L, N)):
+                        xt = X[b, order[t], sl]
+                        k = Bs[1] @ xt
+                        v = Bs[2] @ xt
+                        eta = _sig((Bs[3] @ xt)[0])
+                        alpha = am * _sig((Bs[4] @ xt)[0])
+                        kh = k / np.sqrt(k @ k + LD(eps))
+                        e = kh - v
+                        g = np.sqrt(e @ e) * np.sqrt(kh @ kh)
+                        if cap == "soft":
+                            eta1 = eta if g == 0 else (1 - alpha) * np.tanh(eta * g / (1 - alpha)) / g
+                        elif cap == "hard":
+                            eta1 = eta if g == 0 else min(eta, (1 - alpha) / g)
+                        else:
+                            eta1 = eta
+                        n2 = kh @ kh
+                        eta2 = min(eta1, 2 * alpha / n2) if (clamp and n2 > 0) else eta1
+                        R = alpha * I - eta2 * np.outer(kh, kh)
+                        for i in range(5):
+                            G = np.outer(Bs[i] @ kh - Bs[i] @ v, kh)
+                            mems[i] = mems[i] @ R - eta2 * G
+                        y[b, t, sl] = mems[0] @ Qx[b, order[t], sl]
+        out.append(y)
+    return np.stack(out)
+
+
+def test_l2_gradient_matches_finite_differences():
+    """G = (B k^ - B v) k^T is the gradient of 1/2 |M k^ - B v|^2 at M = B
+    (the private target B v held fixed) [SUMMARY write rule]."""
+    rng = np.random.default_rng(0)
+    d = 5
+    Bm = rng.normal(size=(d, d))
+    kh = rng.normal(size=d)
+    kh /= np.linalg.norm(kh) * 1.3
+    v = rng.normal(size=d)
+    target = Bm @ v
+
+    def loss(M):
+        r = M @ kh - target
+        return 0.5 * r @ r
+
+    G = np.outer(Bm @ kh - Bm @ v, kh)
+    h = 1e-6
+    fd = np.zeros_like(Bm)
+    for i in range(d):
+        for j in range(d):
+            E = np.zeros_like(Bm)
+            E[i, j] = h
+            fd[i, j] = (loss(Bm + E) - loss(Bm - E)) / (2 * h)
+    assert np.allclose(fd, G, rtol=1e-8, atol=1e-9)
+
+
+@pytest.mark.parametrize("H,W", [(2, 2), (2, 3), (3, 2), (3, 3), (4, 4)])
+@pytest.mark.parametrize("chunk", [0, 1, 3, "N"])
+def test_brute_force_tiny_grids(H, W, chunk):
+    d, heads = 4, 2
+    x, st = _wl(H, W, d=d, heads=heads, seed=H * 10 + W, std=0.5, B=1)
+    x = x * 2.0
+    c = H * W if chunk == "N" else chunk
+    y = oracle.scan(x, st, heads, d, 15, chunk_row=c, chunk_col=c)
+    yb = brute_force(x, st, heads, d, 15, chunk_row=c, chunk_col=c).astype(np.float64)
+    scale = np.abs(yb).max()
+    assert scale > 1e-6
+    assert np.abs(y - yb).max() <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("cap,clamp", [("hard", True), ("off", True), ("soft", False)])
+def test_brute_force_variants(cap, clamp):
+    d, heads = 4, 2
+    x, st = _wl(3, 4, d=d, heads=heads, seed=3, std=2.0, B=1)
+    cm = {"soft": oracle.CAP_SOFT, "hard": oracle.CAP_HARD, "off": oracle.CAP_OFF}[cap]
+    y = oracle.scan(x, st, heads, d, 15, cap_mode=cm, clamp=clamp, chunk_row=2, chunk_col=5)
+    yb = brute_force(x, st, heads, d, 15, cap=cap, clamp=clamp, chunk_row=2,
+                     chunk_col=5).astype(np.float64)
+    scale = np.abs(yb).max()
+    assert np.abs(y - yb).max() <= 1e-11 * scale
+
+
+def test_separate_queries_brute_force():
+    d, heads = 4, 1
+    x, st = _wl(3, 3, d=d, heads=heads, seed=9, std=0.5, B=1)
+    q = synth.normals(9, 5, x.size).reshape(x.shape)
+    y = oracle.scan(x, st, heads, d, 15, q=q)
+    yb = brute_force(x, st, heads, d, 15, q=q).astype(np.float64)
+    assert np.abs(y - yb).max() <= 1e-12 * np.abs(yb).max()
+
+
+def test_chunk1_equals_tokenwise_recurrence():
+    """With one-token chunks the boundary is the working state, so the rule is
+    the token-wise recurrence M <- M (alpha I - eta'' k^ k^T) - eta'' M e k^T
+    [SUMMARY stabilisation: token-wise and chunk-wise recurrences]."""
+    d, heads = 4, 1
+    x, st = _wl(3, 4, d=d, heads=heads, seed=21, std=0.7, B=1)
+    y = oracle.scan(x, st, heads, d, 1, chunk_row=1)
+    N = 12
+    X = x.reshape(N, d)
+    s = st[0, 0]
+    M = [s[:16].reshape(4, 4), s[16:32].reshape(4, 4), s[32:48].reshape(4, 4),
+         s[48:52].reshape(1, 4), s[52:56].reshape(1, 4)]
+    ys = np.zeros((N, d))
+    for t in range(N):
+        xt = X[t]
+        k, v = M[1] @ xt, M[2] @ xt
+        eta = 1 / (1 + math.exp(-(M[3] @ xt)[0]))
+        alpha = 0.9 / (1 + math.exp(-(M[4] @ xt)[0]))
+        kh = k / math.sqrt(k @ k + 1e-6)
+        e = kh - v
+        g = np.linalg.norm(e) * np.linalg.norm(kh)
+        eta1 = (1 - alpha) * math.tanh(eta * g / (1 - alpha)) / g
+        eta2 = min(eta1, 2 * alpha / (kh @ kh))
+        T = alpha * np.eye(d) - eta2 * np.outer(kh, kh) - eta2 * np.outer(e, kh)
+        M = [m @ T for m in M]
+        ys[t] = M[0] @ xt
+    assert np.abs(y[0, 0] - ys).max() <= 1e-12 * np.abs(ys).max()
+
+
+def test_zero_input_closed_form():
+    """x = 0: k = v = 0, eta = sigmoid(0) = 1/2, alpha = alpha_max/2, no write,
+    so y_t = (alpha_max/2)^(t+1) M_c,0 q_t along every route."""
+    d, heads, H, W = 4, 2, 3, 5
+    x = np.zeros((1, H, W, heads * d))
+    q = synth.normals(3, 5, x.size).reshape(x.shape)
+    st = synth.states(3, heads, d, 0.5).astype(np.float64)
+    for cr, cc in ((0, 0), (1, 1), (4, 2)):
+        y = oracle.scan(x, st, heads, d, 15, q=q, alpha_max=0.8, chunk_row=cr, chunk_col=cc)
+        for r in range(4):
+            order = _route_order(r, H, W)
+            Q = q.reshape(H * W, heads * d)[order]
+            for h in range(heads):
+                Mc = st[r, h, :d * d].reshape(d, d)
+                f = 0.4 ** (np.arange(H * W) + 1)
+                exp = f[:, None] * (Q[:, h * d:(h + 1) * d] @ Mc.T)
+                assert np.allclose(y[r, 0, :, h * d:(h + 1) * d], exp, rtol=1e-13, atol=0)
+
+
+def test_linearity_in_q_and_content_memory():
+    d, heads = 4, 2
+    x, st = _wl(4, 3, d=d, heads=heads, seed=33, std=0.6, B=1)
+    q1 = synth.normals(33, 5, x.size).reshape(x.shape)
+    q2 = synth.normals(34, 5, x.size).reshape(x.shape)
+    y1 = oracle.scan(x, st, heads, d, 15, q=q1)
+    y2 = oracle.scan(x, st, heads, d, 15, q=q2)
+    y12 = oracle.scan(x, st, heads, d, 15, q=q1 - 3.0 * q2)
+    assert np.allclose(y12, y1 - 3.0 * y2, rtol=0, atol=1e-12 * np.abs(y1).max())
+    st3 = st.copy()
+    st3[:, :, :d * d] *= -2.5      # M_c never feeds keys, values or rates
+    y3 = oracle.scan(x, st3, heads, d, 15, q=q1)
+    assert np.allclose(y3, -2.5 * y1, rtol=0, atol=1e-12 * np.abs(y1).max())
+
+
+# ------------------------------------------------- stability guarantees
+
+def _check_invariants(tr, tol=1e-12):
+    alpha, eta1, eta2, g, nkh = tr[..., 10], tr[..., 12], tr[..., 13], tr[..., 14], tr[..., 15]
+    # soft cap: injection inside the margin 1 - alpha
+    assert np.all(eta2 * g <= (1 - alpha) * (1 + tol) + tol)
+    # spectral clamp: |alpha - eta'' |k^|^2| <= alpha, so |R|_2 <= alpha
+    assert np.all(tr[..., 16] <= alpha * (1 + tol) + tol)
+    assert np.all(eta2 <= eta1 * (1 + tol))
+    # memory norms never exceed the chunk-boundary norms
+    assert np.all(tr[..., 0:5] <= tr[..., 5:10] * (1 + tol) + 1e-300)
+
+
+@pytest.mark.parametrize("std,outliers", [(0.02, 0.0), (0.5, 0.05), (3.0, 0.05), (10.0, 0.1)])
+def test_nonexpansion_random_and_adversarial(std, outliers):
+    wl = synth.make("adv", 1, 9, 11, 32, 2, 16, "f32", 17, state_std=std,
+                    outlier_frac=outliers)
+    for cr, cc in ((0, 0), (1, 1), (5, 7), (99, 99)):
+        _, tr = oracle.scan(wl.x, wl.states, 2, 16, 15, chunk_row=cr, chunk_col=cc, trace=True)
+        _check_invariants(tr)
+        # boundary norms are monotone from one chunk to the next
+        pos = tr[..., 17]
+        bnd = tr[..., 5:10]
+        first = pos == 0
+        for s in range(4):
+            b = bnd[s, 0, 0][first[s, 0, 0]]
+            assert np.all(np.diff(b, axis=0) <= 1e-12 * b[:-1] + 1e-300)
+
+
+def test_clamp_and_cap_are_exercised():
+    wl = synth.make("adv", 1, 9, 11, 32, 2, 16, "f32", 17, state_std=3.0, outlier_frac=0.05)
+    _, tr = oracle.scan(wl.x, wl.states, 2, 16, 15, trace=True)
+    assert (tr[..., 13] < tr[..., 12]).mean() > 0.001      # clamp active
+    assert (tr[..., 12] < 0.99 * tr[..., 11]).mean() > 0.05  # cap active
+
+
+def test_negative_control_without_soft_cap():
+    """Without the injection cap the boundary-relative norm bound breaks on
+    adversarial inputs [SUMMARY stabilisation and ablation paragraphs], so the
+    invariant check above has teeth."""
+    wl = synth.make("adv", 1, 9, 11, 32, 2, 16, "f32", 17, state_std=3.0, outlier_frac=0.1)
+    _, tr = oracle.scan(wl.x, wl.states, 2, 16, 15, cap_mode=oracle.CAP_OFF, trace=True)
+    with pytest.raises(AssertionError):
+        _check_invariants(tr)
+    assert np.any(tr[..., 0:5] > tr[..., 5:10] * 1.01)
+
+
+def test_negative_control_without_clamp():
+    wl = synth.make("adv", 1, 9, 11, 32, 2, 16, "f32", 17, state_std=3.0, outlier_frac=0.1)
+    _, tr = oracle.scan(wl.x, wl.states, 2, 16, 15, clamp=False, trace=True)
+    assert np.any(tr[..., 16] > tr[..., 10] * 1.01)
+
+
+def test_soft_cap_shape():
+    """The cap is smooth, never raises the step, approaches eta as g -> 0 and
+    keeps eta' g below 1 - alpha [OVERVIEW stability controls]."""
+    wl = synth.make("adv", 1, 9, 11, 32, 2, 16, "f32", 17, state_std=1.0, outlier_frac=0.05)
+    _, tr = oracle.scan(wl.x, wl.states, 2, 16, 15, trace=True, clamp=False)
+    alpha, eta, eta1, g = tr[..., 10], tr[..., 11], tr[..., 12], tr[..., 14]
+    assert np.all(eta1 <= eta * (1 + 1e-15))
+    assert np.all(eta1 * g <= (1 - alpha) * (1 + 1e-15))
+    u = eta * g / (1 - alpha)
+    small = u < 1e-2
+    if small.any():
+        assert np.allclose(eta1[small], eta[small] * (1 - u[small] ** 2 / 3), rtol=1e-7)
+    _, trh = oracle.scan(wl.x, wl.states, 2, 16, 15, trace=True, clamp=False,
+                         cap_mode=oracle.CAP_HARD)
+    a, e, e1, gg = trh[..., 10], trh[..., 11], trh[..., 12], trh[..., 14]
+    assert np.allclose(e1, np.minimum(e, (1 - a) / np.maximum(gg, 1e-300)), rtol=1e-15)
+
+
+# ------------------------------------------------------------ Q-form
+
+def qform_scan(x, st, heads, d, route_mask, alpha_max=0.9, eps=1e-6, chunk_row=0, chunk_col=0):
+    """The kernels' rewrite: inside a chunk every memory equals its boundary
+    value times one shared d x d matrix Q (Q = I at the boundary),
+    Q <- alpha Q - eta'' (Q k^ + e) k^T, y_t = B_c (Q q_t), and the boundary
+    refreshes to B Q at the chunk end."""
+    B, H, W, C = x.shape
+    N = H * W
+    X = x.reshape(B, N, C)
+    out = []
+    for r in range(4):
+        if not (route_mask >> r) & 1:
+            continue
+        L = (chunk_row or W) if r < 2 else (chunk_col or H)
+        order = _route_order(r, H, W)
+        y = np.zeros((B, N, C))
+        for b in range(B):
+            for h in range(heads):
+                Mall = st[r, h].reshape(3 * d + 2, d).copy()
+                sl = slice(h * d, (h + 1) * d)
+                for c0 in range(0, N, L):
+                    Bn = Mall.copy()
+                    Q = np.eye(d)
+                    for t in range(c0, min(c0 + L, N)):
+                        xt = X[b, order[t], sl]
+                        k = Bn[d:2 * d] @ xt
+                        v = Bn[2 * d:3 * d] @ xt
+                        eta = 1 / (1 + math.exp(-(Bn[3 * d] @ xt)))
+                        alpha = alpha_max / (1 + math.exp(-(Bn[3 * d + 1] @ xt)))
+                        kh = k / math.sqrt(k @ k + eps)
+                        e = kh - v
+                        g = np.linalg.norm(e) * np.linalg.norm(kh)
+                        eta1 = eta if g == 0 else (1 - alpha) * math.tanh(eta * g / (1 - alpha)) / g
+                        eta2 = min(eta1, 2 * alpha / (kh @ kh)) if kh @ kh > 0 else eta1
+                        Q = alpha * Q - eta2 * np.outer(Q @ kh + e, kh)
+                        y[b, t, sl] = Bn[:d] @ (Q @ xt)
+                    Mall = Bn @ Q
+        out.append(y)
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 5])
+def test_qform_equals_five_memory_form(chunk):
+    x, st = _wl(6, 5, d=8, heads=2, seed=41, std=0.4, B=1)
+    y = oracle.scan(x, st, 2, 8, 15, chunk_row=chunk, chunk_col=chunk)
+    yq = qform_scan(x, st, 2, 8, 15, chunk_row=chunk, chunk_col=chunk)
+    assert np.abs(y - yq).max() <= 1e-12 * np.abs(y).max()
+
+
+# ------------------------------------------------------------ fusion
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 5, 10, 15])
+def test_fuse_restores_and_weights(mask):
+    B, H, W, C = 2, 3, 5, 6
+    R = bin(mask).count("1")
+    y = synth.normals(2, 1, R * B * H * W * C).reshape(R, B, H * W, C)
+    sc = synth.scales(2, C).astype(np.float64)
+    out = oracle.fuse(y, B, H, W, C, mask, sc)
+    exp = np.zeros((B, H * W, C))
+    slot = 0
+    for r in range(4):
+        if not (mask >> r) & 1:
+            continue
+        inv = np.argsort(_route_order(r, H, W))     # grid cell -> token
+        exp = exp + sc[r] * y[slot][:, inv, :]
+        slot += 1
+    assert np.allclose(out.reshape(B, H * W, C), exp, rtol=1e-15, atol=1e-15)
+    if R == 1:  # a single route with unit scales is a pure restore, exactly
+        ones = np.ones((4, C))
+        out1 = oracle.fuse(y, B, H, W, C, mask, ones)
+        r = int(math.log2(mask))
+        inv = np.argsort(_route_order(r, H, W))
+        assert np.array_equal(out1.reshape(B, H * W, C), y[0][:, inv, :])
+
+
+def test_oracle_rejects_bad_arguments():
+    x, st = _wl(2, 2, d=4, heads=2, B=1)
+    for kw in (dict(route_mask=0), dict(route_mask=16), dict(alpha_max=1.0),
+               dict(alpha_max=0.0), dict(eps=0.0), dict(chunk_row=-1)):
+        rm = kw.pop("route_mask", 15)
+        with pytest.raises(ValueError):
+            oracle.scan(x, st, 2, 4, rm, **kw)
+    with pytest.raises(ValueError):   # C != heads * d
+        oracle.scan(x, st, 3, 4, 15)
