@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the four-route SRNL forward pass on one MI355X.
+
+One step = srnl_scan_fwd (route gather, boundary generation, transition
+scalars, token-order update, readout: all four routes) + srnl_fuse (restore and
+channel-scale fusion) over one batch of the hierarchical stage-1 grid:
+B=64, 56x56, C=64, 2 heads of d=32, chunk 56, bf16 input, fp32 state, rows
+AR(1)-correlated (rho = 0.9), seed 2. Inputs are synthetic (synth.hier56) and
+resident in HBM before the timed region.
+
+Prints one JSON line with the throughput in tokens*heads/s, the roofline of
+the dominant kernel (the scan kernel), and a CPU baseline: the oracle timed on
+a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SRNL fwd tokens·heads/s (4 routes) at stage shapes; % of HBM/MFMA roofline"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "scan_kernel_hier56_traffic.json")
+SRC = os.path.join(ROOT, "self_referential_memory_amd", "csrc", "srnl.hip")
+
+# Published MI355X peaks used for the roofline.
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_flops_per_unit(d: int) -> int:
+    """Work per token x head x route of the plain five-memory form, with a
+    fused multiply-add counted as 2 flops: generation and learning signals
+    10 d^2 + 8 d (dense contractions) plus the token-order update and readout
+    17 d^2 + 20 d."""
+    return (10 * d * d + 8 * d) + (17 * d * d + 20 * d)
+
+
+def src_sha() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launches_units: int):
+    """HBM bytes per scan launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != src_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_items: int):
+    import numpy as np
+    import oracle
+    sample = wl.x[:n_items]
+    t0 = time.perf_counter()
+    y = oracle.scan(sample, wl.states, wl.heads, wl.d, 15, alpha_max=wl.alpha_max, eps=wl.eps)
+    oracle.fuse(y, n_items, wl.H, wl.W, wl.C, 15, wl.scales)
+    dt = time.perf_counter() - t0
+    units = n_items * wl.H * wl.W * wl.heads
+    return {"value": units / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch items 0..{n_items - 1} of {wl.B} (all 4 routes, {wl.heads} heads, "
+                      f"{wl.H}x{wl.W}), scan + fuse, single-threaded double precision, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-items", type=int, default=16,
+                    help="batch items the CPU-baseline oracle runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (PMC calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator's chains are independent and would shard over batch, "
+              "heads and routes without communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from self_referential_memory_amd import srnl, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.hier56()
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(dev)
+    sc = torch.from_numpy(wl.scales).to(dev)
+    R = 4
+    y = torch.empty((R, wl.B, wl.N, wl.C), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.bfloat16, device=dev)
+    p = srnl.make_params(st, x, alpha_max=wl.alpha_max, eps=wl.eps)
+
+    def step(ev_a=None, ev_b=None):
+        if ev_a is not None:
+            ev_a.record()
+        srnl.scan_fwd(x, st, wl.heads, wl.d, 15, out=y, params=p)
+        if ev_b is not None:
+            ev_b.record()
+        srnl.fuse(y, wl.B, wl.H, wl.W, wl.C, 15, sc, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms = dt * 1000.0 / args.steps
+    units = wl.B * wl.H * wl.W * wl.heads            # tokens x heads per step
+    value = units / (ms / 1000.0)
+    thr_units = units * R                            # tokens x heads x routes per launch
+    flops = algorithmic_flops_per_unit(wl.d) * thr_units
+    achieved = flops / (scan_ms / 1000.0) / 1e12
+    traffic = traffic_from_profile(thr_units)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "hier56: SRNL forward over the hierarchical stage-1 grid, B=64, "
+                        "56x56, C=64, 2 heads x d=32, 4 routes, chunk 56 (rows) / 56 "
+                        "(columns), bf16 input, fp32 state and arithmetic, AR(1) rows "
+                        "rho=0.9, seed 2",
+            "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads, "d": wl.d,
+            "routes": R, "input_dtype": "bf16", "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "scan_kernel",
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_VALU_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+            "traffic": traffic,
+            "scan_ms": scan_ms,
+            "algorithmic_flops_per_launch": flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_items)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * srnl.h -- C ABI of libsrnl.so: the forward pass of the stabilised SRNL
+ * operator over a 2-D feature grid (four routes, row/column-aligned chunks,
+ * learned channel-scale fusion) on AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [README]   "VisionHOPE" README (github.com/PSRben/VisionHOPE), sections
+ *              "Overview", "SRNL and VisionHOPE operator", "Fast inference".
+ *   [OVERVIEW] "VisionHOPE Model Overview: Architecture, Benchmarks, and
+ *              Practical Limits", sections "How VisionHOPE's Five Memories
+ *              Work", "Four-Directional Scanning and Spatial Chunking", "Why
+ *              the Stability Controls Matter", "Fast Inference, Mixed
+ *              Precision, and Evaluation", "Practical Limitations and Common
+ *              Pitfalls".
+ *   [SUMMARY]  "VisionHOPE: Visual Backbones as Self-Modifying Learning
+ *              Systems" (arXiv 2609.33325 summary), paragraphs on the write
+ *              rule, on stabilisation, on 2-D maps and on the ablations.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are device pointers (HBM) unless a comment says "host". The
+ *     caller allocates and owns every buffer; the library never allocates,
+ *     frees or synchronises, and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously: a return of SRNL_OK means the arguments were
+ *     valid and the kernels were launched.
+ *   - Grids are NHWC: x[b][i][j][c], c fastest. Head h owns channels
+ *     [h*d, (h+1)*d) [README SRNL and VisionHOPE operator].
+ *   - Errors are returned as srnl_status; nothing throws across the ABI.
+ *     srnl_last_error() gives a thread-local human-readable detail.
+ *   - Empty grids (B, H or W equal to 0) are valid and launch nothing.
+ */
+#ifndef SRNL_H
+#define SRNL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SRNL_OK = 0,
+    SRNL_ERR_ARG = -1,       /* a size, mask, head_dim or scalar is invalid */
+    SRNL_ERR_DTYPE = -2,     /* unknown dtype */
+    SRNL_ERR_PTR = -3,       /* NULL, or not device memory where required */
+    SRNL_ERR_HIP = -5        /* a HIP runtime call or launch failed */
+} srnl_status;
+
+typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
+
+/* Routes, in the order the pages list them [OVERVIEW Four-Directional
+ * Scanning and Spatial Chunking]: bit 0 forward row-major, bit 1 reverse
+ * row-major, bit 2 forward column-major, bit 3 reverse column-major. A
+ * reverse route visits the whole sequence of its forward route backwards. */
+#define SRNL_ROUTE_ROW      1u
+#define SRNL_ROUTE_ROW_REV  2u
+#define SRNL_ROUTE_COL      4u
+#define SRNL_ROUTE_COL_REV  8u
+#define SRNL_ROUTES_ALL     15u
+
+/* Variant flags for srnl_params.flags. 0 is the operator as described:
+ * soft injection cap, spectral clamp, retention from the retention memory,
+ * readout after each token's write. The others are the ablations named in
+ * [SUMMARY ablation paragraph] and alternative readings. */
+#define SRNL_FLAG_HARD_CAP     0x1u  /* hard injection clamp min(eta, (1-alpha)/g) */
+#define SRNL_FLAG_NO_CAP       0x2u  /* no injection cap */
+#define SRNL_FLAG_NO_CLAMP     0x4u  /* no spectral clamp */
+#define SRNL_FLAG_FIXED_ALPHA  0x8u  /* alpha = alpha_max for every token */
+#define SRNL_FLAG_READ_BEFORE  0x10u /* y_t read before token t's write */
+
+/* Floats of initial state per (route, head): 3d^2 + 2d. */
+#define SRNL_STATE_FLOATS(d) (3 * (d) * (d) + 2 * (d))
+
+typedef struct {
+    /* Learned initial states [README SRNL and VisionHOPE operator; OVERVIEW
+     * How VisionHOPE's Five Memories Work], fp32, device,
+     * [4 routes][heads][3d^2+2d]: M_c, M_k, M_v (row-major d x d), then
+     * m_eta, m_alpha (length d). All four routes' slots are present even if
+     * route_mask leaves some out. Every call starts from these states: each
+     * forward pass begins a new sequence. */
+    const float *states;
+    /* Queries, same shape and dtype as x, or NULL for q = x [README SRNL and
+     * VisionHOPE operator]. */
+    const void *q;
+    srnl_dtype in_dtype;  /* dtype of x and q; state and arithmetic are fp32 */
+    float alpha_max;      /* retention ceiling, in (0, 1); alpha = alpha_max * sigmoid(m_alpha . x) */
+    float eps;            /* > 0; key normalisation k / sqrt(|k|^2 + eps) */
+    int chunk_row;        /* 0: chunk = W on row routes; > 0: that length (last chunk may be short) */
+    int chunk_col;        /* 0: chunk = H on column routes; > 0: that length */
+    unsigned flags;       /* SRNL_FLAG_* */
+    void *stream;         /* hipStream_t */
+} srnl_params;
+
+/*
+ * srnl_scan_fwd -- the SRNL scan along the active routes.
+ *
+ * Computes, for every active route r, batch b and head h, independently
+ * [OVERVIEW Four-Directional Scanning and Spatial Chunking; SUMMARY 2-D
+ * maps]: tokens are visited in route order; at each chunk boundary the
+ * boundary states generate every token's key k = B_k x, value v = B_v x,
+ * step size eta = sigmoid(b_eta . x) and retention alpha = alpha_max *
+ * sigmoid(b_alpha . x); keys are normalised k^ = k / sqrt(|k|^2 + eps); the
+ * step is soft-capped with the key-value discrepancy e = k^ - v and margin
+ * 1 - alpha, then clamped to 2 alpha / |k^|^2 so the retained transition
+ * stays within alpha [SUMMARY stabilisation; OVERVIEW Why the Stability
+ * Controls Matter]; inside the chunk the five working memories update in
+ * token order by retained delta gradient descent, M <- alpha M - eta''
+ * (M k^ + B e) k^T [SUMMARY write rule]; the readout is y_t = M_c q_t after
+ * the write.
+ *
+ *   x     [B][H][W][C], in_dtype, device. C must equal heads * d.
+ *   d     head dim, one of 4, 8, 16, 32, 64 [README SRNL and VisionHOPE
+ *         operator].
+ *   route_mask  1..15 (SRNL_ROUTE_*).
+ *   out   [R][B][H*W][C] fp32, device, R = popcount(route_mask): slot s
+ *         holds the s-th active route (ascending bit order), tokens in
+ *         that route's traversal order. Fully overwritten.
+ * Errors: SRNL_ERR_ARG (C != heads*d, d not allowed, mask out of range,
+ * negative sizes, alpha_max not in (0,1), eps <= 0, negative chunk,
+ * sizes whose element counts overflow), SRNL_ERR_DTYPE, SRNL_ERR_PTR
+ * (x, out or params->states NULL or not device memory; q not device
+ * memory), SRNL_ERR_HIP.
+ */
+srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
+                          int d, unsigned route_mask, const srnl_params *params,
+                          float *out);
+
+/*
+ * srnl_fuse -- restore and fuse [OVERVIEW Four-Directional Scanning and
+ * Spatial Chunking; SUMMARY 2-D maps]: each route's outputs go back to
+ * their grid cells and are combined with learned per-channel scales,
+ *   out[b][i][j][c] = sum over active r, ascending, of
+ *                     scales[r][c] * y[slot(r)][b][t_r(i,j)][c]
+ * where t_r(i,j) is the step at which route r visits cell (i, j).
+ *
+ *   y_routes  [R][B][H*W][C] fp32 as written by srnl_scan_fwd.
+ *   scales    [4][C] fp32 (rows of inactive routes are ignored).
+ *   out       [B][H][W][C] in out_dtype (bf16: round to nearest even).
+ * Errors: SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_HIP.
+ */
+srnl_status srnl_fuse(const float *y_routes, int B, int H, int W, int C,
+                      unsigned route_mask, const float *scales,
+                      srnl_dtype out_dtype, void *out, void *stream);
+
+/*
+ * srnl_route_gather -- the route traversal as a standalone copy [OVERVIEW
+ * Four-Directional Scanning and Spatial Chunking]:
+ *   out[slot(r)][b][t][c] = x[b][i][j][c],  (i, j) = route r's t-th cell.
+ * srnl_scan_fwd performs the same gather inside its load stage; this entry
+ * point exposes it for callers (and for bit-exact checks).
+ *   x    [B][H][W][C] in dtype;  out  [R][B][H*W][C] in dtype.
+ * Errors: SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_HIP.
+ */
+srnl_status srnl_route_gather(const void *x, int B, int H, int W, int C,
+                              unsigned route_mask, srnl_dtype dtype, void *out,
+                              void *stream);
+
+/*
+ * srnl_init_states -- fill the learned-initial-state buffer [README SRNL
+ * and VisionHOPE operator; OVERVIEW How VisionHOPE's Five Memories Work]
+ * with std * N(0,1) entries, deterministically from `seed`:
+ *   states  [4][heads][3d^2+2d] fp32, device.
+ * Entry n is normal n of stream 2 of the counter-based generator
+ * Philox4x32-10 (Salmon et al., SC'11) keyed by seed: block k uses counter
+ * (k mod 2^32, k div 2^32, 2, 0x53524E4C); its words a0..a3 give
+ * u(a) = (a + 0.5) 2^-32 and, by Box-Muller in double precision, normals
+ * 4k..4k+3 = r0 cos t0, r0 sin t0, r1 cos t1, r1 sin t1 with
+ * r = sqrt(-2 ln u(a0 or a2)), t = 2 pi u(a1 or a3).
+ * Errors: SRNL_ERR_ARG (heads < 1, d not allowed, std < 0 or not finite),
+ * SRNL_ERR_PTR, SRNL_ERR_HIP.
+ */
+srnl_status srnl_init_states(float *states, int heads, int d,
+                             unsigned long long seed, float std, void *stream);
+
+/* Host helpers (no device work). */
+
+/* Cell (i, j) visited at step t of route r (0..3) on an H x W grid; host. */
+void srnl_route_index(int r, int H, int W, long t, int *i, int *j);
+/* Chunk length route r uses: W or H unless the override is > 0; host. */
+int srnl_chunk_len(int r, int H, int W, int chunk_row, int chunk_col);
+const char *srnl_status_string(srnl_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char *srnl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SRNL_H */

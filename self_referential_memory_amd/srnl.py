@@ -1,0 +1,175 @@
+"""Thin ctypes binding over libsrnl.so (C ABI in include/srnl.h).
+
+Argument marshalling only: tensors are passed as device pointers with the
+caller's current HIP stream; every step of the operator runs in the library's
+kernels. The library must be built (``python -m
+self_referential_memory_amd.build`` or ``__graft_entry__.build()``); loading
+fails loudly when it is missing. There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsrnl.so")
+
+SRNL_OK, SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_HIP = 0, -1, -2, -3, -5
+SRNL_F32, SRNL_BF16 = 0, 1
+FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = (
+    0x1, 0x2, 0x4, 0x8, 0x10)
+
+EXPORTS = ("srnl_scan_fwd", "srnl_fuse", "srnl_route_gather", "srnl_init_states",
+           "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
+           "srnl_last_error")
+
+
+class SrnlError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("states", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("in_dtype", ctypes.c_int), ("alpha_max", ctypes.c_float),
+                ("eps", ctypes.c_float), ("chunk_row", ctypes.c_int),
+                ("chunk_col", ctypes.c_int), ("flags", ctypes.c_uint),
+                ("stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsrnl.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
+        L.srnl_scan_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp]
+        L.srnl_fuse.argtypes = [vp, i, i, i, i, u, vp, i, vp, vp]
+        L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
+        L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
+        for f in ("srnl_scan_fwd", "srnl_fuse", "srnl_route_gather", "srnl_init_states"):
+            getattr(L, f).restype = ctypes.c_int
+        L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
+                                       ctypes.POINTER(i)]
+        L.srnl_route_index.restype = None
+        L.srnl_chunk_len.argtypes = [i, i, i, i, i]
+        L.srnl_chunk_len.restype = ctypes.c_int
+        L.srnl_status_string.argtypes = [i]
+        L.srnl_status_string.restype = ctypes.c_char_p
+        L.srnl_last_error.argtypes = []
+        L.srnl_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != SRNL_OK:
+        raise SrnlError(status, where, lib().srnl_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SRNL_F32
+    if t.dtype == torch.bfloat16:
+        return SRNL_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def route_index(r: int, H: int, W: int, t: int):
+    i, j = ctypes.c_int(), ctypes.c_int()
+    lib().srnl_route_index(r, H, W, t, ctypes.byref(i), ctypes.byref(j))
+    return i.value, j.value
+
+
+def chunk_len(r: int, H: int, W: int, chunk_row: int = 0, chunk_col: int = 0) -> int:
+    return lib().srnl_chunk_len(r, H, W, chunk_row, chunk_col)
+
+
+def make_params(states: torch.Tensor, x: torch.Tensor, q: Optional[torch.Tensor] = None, *,
+                alpha_max: float = 0.9, eps: float = 1e-6, chunk_row: int = 0,
+                chunk_col: int = 0, flags: int = 0, stream=None) -> Params:
+    return Params(_ptr(states), _ptr(q), _dtype_code(x), alpha_max, eps, chunk_row,
+                  chunk_col, flags, _stream(stream))
+
+
+def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
+             route_mask: int = 15, q: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, *, params: Optional[Params] = None,
+             **kw) -> torch.Tensor:
+    """srnl_scan_fwd: x [B,H,W,C] -> per-route outputs [R,B,H*W,C] fp32."""
+    B, H, W, C = x.shape
+    R = bin(route_mask & 15).count("1")
+    if out is None:
+        out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
+    p = params if params is not None else make_params(states, x, q, **kw)
+    _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
+                               ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
+    return out
+
+
+def fuse(y: torch.Tensor, B: int, H: int, W: int, C: int, route_mask: int,
+         scales: torch.Tensor, out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+         stream=None) -> torch.Tensor:
+    """srnl_fuse: per-route outputs -> restored, channel-scaled sum [B,H,W,C]."""
+    if out is None:
+        out = torch.empty((B, H, W, C), dtype=out_dtype, device=y.device)
+    _check(lib().srnl_fuse(_ptr(y), B, H, W, C, route_mask, _ptr(scales),
+                           _dtype_code(out), _ptr(out), _stream(stream)), "srnl_fuse")
+    return out
+
+
+def route_gather(x: torch.Tensor, route_mask: int = 15, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """srnl_route_gather: x [B,H,W,C] -> [R,B,H*W,C] in route order."""
+    B, H, W, C = x.shape
+    R = bin(route_mask & 15).count("1")
+    if out is None:
+        out = torch.empty((R, B, H * W, C), dtype=x.dtype, device=x.device)
+    _check(lib().srnl_route_gather(_ptr(x), B, H, W, C, route_mask, _dtype_code(x),
+                                   _ptr(out), _stream(stream)), "srnl_route_gather")
+    return out
+
+
+def init_states(heads: int, d: int, seed: int, std: float, device="cuda",
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """srnl_init_states: [4, heads, 3d^2+2d] fp32 ~ std * N(0,1) (Philox)."""
+    if out is None:
+        out = torch.empty((4, heads, 3 * d * d + 2 * d), dtype=torch.float32, device=device)
+    _check(lib().srnl_init_states(_ptr(out), heads, d, seed, std, _stream(stream)),
+           "srnl_init_states")
+    return out
+
+
+def forward(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: int, d: int,
+            route_mask: int = 15, q: Optional[torch.Tensor] = None, out_dtype=None,
+            **kw) -> torch.Tensor:
+    """Scan + fuse: the operator's forward pass on an NHWC grid."""
+    B, H, W, C = x.shape
+    y = scan_fwd(x, states, heads, d, route_mask, q, **kw)
+    return fuse(y, B, H, W, C, route_mask, scales,
+                out_dtype=x.dtype if out_dtype is None else out_dtype,
+                stream=kw.get("stream"))

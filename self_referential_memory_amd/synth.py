@@ -108,10 +108,13 @@ def state_size(d: int) -> int:
 
 
 def states(seed: int, heads: int, d: int, std: float) -> np.ndarray:
-    """Initial memories [4][heads][3d^2+2d] fp32, each entry std * N(0,1)."""
+    """Initial memories [4][heads][3d^2+2d] fp32, each entry std * N(0,1).
+    std is taken at fp32 precision and the product formed in double, then
+    rounded to fp32, as the library's state initialiser does."""
     n = 4 * heads * state_size(d)
     z = normals(seed, STREAM_STATES, n)
-    return (np.float64(std) * z).astype(np.float32).reshape(4, heads, state_size(d))
+    s = np.float64(np.float32(std))
+    return (s * z).astype(np.float32).reshape(4, heads, state_size(d))
 
 
 def scales(seed: int, C: int, lo: float = 0.5, hi: float = 1.5) -> np.ndarray:

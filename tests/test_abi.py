@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/srnl.h declares, its host helpers agree with the oracle's route and
+chunk definitions, and invalid arguments return their documented status
+before any device work."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+from self_referential_memory_amd import srnl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "srnl.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(srnl_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for f in ("srnl_scan_fwd", "srnl_fuse", "srnl_init_states", "srnl_route_gather"):
+        assert f in names
+    assert sorted(srnl.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = srnl.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("H,W", [(1, 1), (2, 3), (14, 20), (7, 56), (200, 304)])
+def test_route_index_matches_oracle(H, W):
+    N = H * W
+    ts = range(N) if N <= 4096 else list(range(0, N, 97)) + [N - 1]
+    for r in range(4):
+        for t in ts:
+            assert srnl.route_index(r, H, W, t) == oracle.route_index(r, H, W, t)
+
+
+def test_chunk_len_matches_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "chunking.json")))
+    for case in g["cases"]:
+        H, W, cr, cc = case["H"], case["W"], case["chunk_row"], case["chunk_col"]
+        assert srnl.chunk_len(0, H, W, cr, cc) == case["row_chunk_len"]
+        assert srnl.chunk_len(3, H, W, cr, cc) == case["col_chunk_len"]
+
+
+def _scan(x=0, B=1, H=2, W=2, C=8, heads=2, d=4, mask=15, **kw):
+    p = srnl.Params(None, None, kw.pop("in_dtype", 0), kw.pop("alpha_max", 0.9),
+                    kw.pop("eps", 1e-6), kw.pop("chunk_row", 0), kw.pop("chunk_col", 0),
+                    kw.pop("flags", 0), None)
+    return srnl.lib().srnl_scan_fwd(x, B, H, W, C, heads, d, mask, ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=5, C=10), srnl.SRNL_ERR_ARG),          # head_dim not in {4,8,16,32,64}
+    (dict(d=128, heads=1, C=128), srnl.SRNL_ERR_ARG),
+    (dict(C=12), srnl.SRNL_ERR_ARG),                # C != heads * d
+    (dict(heads=0, C=0), srnl.SRNL_ERR_ARG),
+    (dict(mask=0), srnl.SRNL_ERR_ARG),
+    (dict(mask=16), srnl.SRNL_ERR_ARG),
+    (dict(B=-1), srnl.SRNL_ERR_ARG),
+    (dict(H=-2), srnl.SRNL_ERR_ARG),
+    (dict(alpha_max=1.0), srnl.SRNL_ERR_ARG),
+    (dict(alpha_max=0.0), srnl.SRNL_ERR_ARG),
+    (dict(alpha_max=float("nan")), srnl.SRNL_ERR_ARG),
+    (dict(eps=0.0), srnl.SRNL_ERR_ARG),
+    (dict(eps=float("inf")), srnl.SRNL_ERR_ARG),
+    (dict(chunk_row=-1), srnl.SRNL_ERR_ARG),
+    (dict(flags=0x100), srnl.SRNL_ERR_ARG),
+    (dict(in_dtype=7), srnl.SRNL_ERR_DTYPE),
+    (dict(B=1 << 30, H=1 << 15, W=1 << 15, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # overflow
+    (dict(B=1, H=1 << 16, W=1 << 16, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # H*W > INT_MAX
+])
+def test_scan_argument_errors(kw, status):
+    assert _scan(**kw) == status
+    assert srnl.lib().srnl_last_error().decode() != ""
+
+
+def test_null_params_is_pointer_error():
+    assert srnl.lib().srnl_scan_fwd(0, 1, 2, 2, 8, 2, 4, 15, None, None) == srnl.SRNL_ERR_PTR
+
+
+def test_empty_grid_is_a_no_op():
+    # nothing to compute: valid, returns before touching any pointer
+    assert _scan(B=0) == srnl.SRNL_OK
+    assert _scan(H=0) == srnl.SRNL_OK
+    assert srnl.lib().srnl_fuse(None, 0, 4, 4, 8, 15, None, 0, None, None) == srnl.SRNL_OK
+    assert srnl.lib().srnl_route_gather(None, 3, 0, 4, 8, 15, 0, None, None) == srnl.SRNL_OK
+
+
+def test_fuse_and_gather_argument_errors():
+    L = srnl.lib()
+    assert L.srnl_fuse(None, 1, 2, 2, 6, 15, None, 0, None, None) == srnl.SRNL_ERR_ARG  # C % 4
+    assert L.srnl_fuse(None, 1, 2, 2, 8, 0, None, 0, None, None) == srnl.SRNL_ERR_ARG
+    assert L.srnl_fuse(None, 1, 2, 2, 8, 15, None, 3, None, None) == srnl.SRNL_ERR_DTYPE
+    assert L.srnl_route_gather(None, 1, 2, 2, 8, 31, 0, None, None) == srnl.SRNL_ERR_ARG
+    assert L.srnl_route_gather(None, 1, 2, 2, 8, 15, 9, None, None) == srnl.SRNL_ERR_DTYPE
+    assert L.srnl_init_states(None, 0, 4, 0, 0.02, None) == srnl.SRNL_ERR_ARG
+    assert L.srnl_init_states(None, 1, 6, 0, 0.02, None) == srnl.SRNL_ERR_ARG
+    assert L.srnl_init_states(None, 1, 4, 0, -1.0, None) == srnl.SRNL_ERR_ARG
+
+
+def test_status_strings():
+    L = srnl.lib()
+    for s in (0, -1, -2, -3, -5):
+        assert L.srnl_status_string(s).decode() not in ("", "unknown status")
