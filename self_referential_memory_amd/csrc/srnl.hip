@@ -14,7 +14,8 @@
 //              maps.
 //
 // Kernel map:
-//   scan_kernel    one workgroup per chain (route, batch, head). Per chunk:
+//   scan_mfma_kernel (d = 32, 64) and scan_simple_kernel (d = 4, 8, 16):
+//                  one workgroup per chain (route, batch, head). Per chunk:
 //                  gathers the chunk's tokens along the route (the route
 //                  gather fused into the load), generates every token's key,
 //                  value, step and retention from the boundary states,
@@ -134,7 +135,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks)
     return (bid & 7) * per + (bid >> 3);
 }
 
-// ------------------------------------------------------------ scan kernel
+// ------------------------------------------------------------ scan kernel, d <= 16
+//
+// Plain VALU version for the small head dims: every contraction is a loop
+// over LDS, one output per thread.
 
 template <int D> struct ScanCfg {
     static constexpr int NT = (4 * D < 64) ? 64 : 4 * D;  // threads per workgroup
@@ -151,7 +155,7 @@ enum : unsigned {
 };
 
 template <int D, typename InT>
-__global__ __launch_bounds__(ScanCfg<D>::NT) void scan_kernel(
+__global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
@@ -378,6 +382,404 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_kernel(
     }
 }
 
+// ------------------------------------------------------------ scan kernel, d = 32, 64
+//
+// One workgroup of 4d threads per chain; T tokens per sub-block (a chunk is
+// processed in sub-blocks of at most T tokens: generation inside a chunk
+// reads only the fixed boundary states, so it may be split).
+//
+//   load      tokens of the next sub-block are prefetched into registers
+//             (16-byte loads along the route) while the current one computes
+//   generate  [k | v] = X B_[k|v]^T on MFMA (v_mfma_f32_16x16x4f32)
+//   epilogue  4 lanes per token: |k|^2, b_eta . x, b_alpha . x, k^, e, the
+//             soft cap and the spectral clamp (quad DPP reductions)
+//   update    4 lanes per row of Q = cq * P, d/4 columns per lane; the
+//             retention factors accumulate in the scalar cq so the write is
+//             one FMA per element: P <- P - (eta''/cq') (cq P k^ + e) k^T
+//   readout   Y = Z B_c^T on MFMA, z_t = Q_t q_t
+//   refresh   B <- B Q_L on MFMA (the two vector memories on VALU)
+//
+// MFMA 16x16x4 f32 operand layout (lane l): A[l%16][l/16], B[l/16][l%16],
+// D[4(l/16)+r][l%16] in accumulator register r. Every operand is read from
+// an LDS array stored [m or n][k] with row stride d+2, which puts the 64
+// lanes of one read on distinct banks.
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int D, int T> struct MCfg {
+    static constexpr int NT = 4 * D;               // threads: 4 lanes per row of Q
+    static constexpr int NW = NT / 64;             // waves
+    static constexpr int ROWS = 3 * D + 2;
+    static constexpr int LDP = D + 2;              // operand row stride
+    static constexpr int CPL = D / 4;              // Q columns per lane
+    static constexpr int KS = D / 4;               // MFMA K-steps over d
+    static constexpr int RT = (3 * D / 16) * (D / 16);  // refresh tiles (matrix rows)
+    static constexpr int RTW = RT / NW;            // refresh tiles per wave
+    static_assert(RT % NW == 0, "refresh tiles must split evenly over waves");
+    static_assert(T % 16 == 0, "T must be a multiple of 16");
+};
+
+// 16-byte vector of input elements
+template <typename InT> struct InVec { static constexpr int VE = 16 / sizeof(InT); };
+
+__device__ __forceinline__ void unpack(const uint4 &w, float (&f)[4], const float *)
+{
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+}
+__device__ __forceinline__ void unpack(const uint4 &w, float (&f)[8], const uint16_t *)
+{
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __uint_as_float(a[k] << 16);
+        f[2 * k + 1] = __uint_as_float(a[k] & 0xFFFF0000u);
+    }
+}
+
+constexpr float kTinyScale = 8.673617379884035e-19f;   // 2^-60
+
+template <int D, int T, typename InT>
+__global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
+    const InT *__restrict__ x, const InT *__restrict__ q,
+    const float *__restrict__ states, float *__restrict__ out, int B, int H,
+    int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
+    float eps, int chunk_row, int chunk_col, unsigned flags, int nchains)
+{
+    using Cfg = MCfg<D, T>;
+    constexpr int NT = Cfg::NT, NW = Cfg::NW, ROWS = Cfg::ROWS, LDP = Cfg::LDP,
+                  CPL = Cfg::CPL, KS = Cfg::KS, RTW = Cfg::RTW;
+    constexpr int VE = InVec<InT>::VE;
+    constexpr int SEGS = D / VE;                       // 16-byte segments per token
+    constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
+
+    __shared__ __align__(16) float Bs[ROWS * LDP];     // boundary rows M_c, M_k, M_v, m_eta, m_alpha
+    __shared__ __align__(16) float Xs[T * LDP];        // x_t (MFMA operand)
+    __shared__ __align__(16) float QVa[T * D];         // q_t (token loop)
+    __shared__ __align__(16) float KZ[T * LDP];        // k (generation), then z_t (readout)
+    __shared__ __align__(16) float Es[T * LDP];        // v, then e = k^ - v
+    __shared__ __align__(16) float KHa[T * D];         // k^ (token loop)
+    __shared__ __align__(16) float2 Sae[T];            // (alpha_t, eta''_t)
+    __shared__ __align__(16) float Qt[D * LDP];        // Q_L^T at the chunk end
+
+    const int chain = xcd_remap(blockIdx.x, gridDim.x);
+    if (chain >= nchains)
+        return;
+    const int slot = chain % R;
+    const int bh = chain / R;
+    const int h = bh % heads;
+    const int b = bh / heads;
+    const int r = nth_route(route_mask, slot);
+    const long long N = static_cast<long long>(H) * W;
+    long long L = (r < 2) ? (chunk_row > 0 ? chunk_row : W)
+                          : (chunk_col > 0 ? chunk_col : H);
+    if (L > N)
+        L = N;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lm = lane & 15, lk = lane >> 4;        // MFMA operand row / k slot
+    const int row = tid >> 2, part = tid & 3;         // token-loop row of Q and column part
+
+    const float *st = states + (static_cast<size_t>(r) * heads + h) * (ROWS * D);
+    for (int idx = tid; idx < ROWS * D; idx += NT)
+        Bs[(idx / D) * LDP + idx % D] = st[idx];
+
+    const size_t xbase = static_cast<size_t>(b) * H * W * C + static_cast<size_t>(h) * D;
+    uint4 pre[NPF], preq[NPF];
+    auto issue_loads = [&](long long s, int n) {
+#pragma unroll
+        for (int k = 0; k < NPF; ++k) {
+            const int seg = tid + k * NT;
+            if (seg < n * SEGS) {
+                const int u = seg / SEGS, sg = seg % SEGS;
+                int i, j;
+                route_cell(r, H, W, N, s + u, i, j);
+                const size_t off = xbase + (static_cast<size_t>(i) * W + j) * C + sg * VE;
+                pre[k] = *reinterpret_cast<const uint4 *>(x + off);
+                if (q)
+                    preq[k] = *reinterpret_cast<const uint4 *>(q + off);
+            }
+        }
+    };
+
+    float P[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        P[c] = (part * CPL + c == row) ? 1.0f : 0.0f;
+    float cq = 1.0f;
+
+    const size_t out_base = static_cast<size_t>(slot) * B + b;
+    const bool before = (flags & F_READ_BEFORE) != 0;
+
+    long long c0 = 0;
+    long long cend = (L < N) ? L : N;
+    long long s0 = 0;
+    int nt = static_cast<int>((T < cend) ? T : cend);
+    issue_loads(s0, nt);
+
+    while (true) {
+        __syncthreads();   // previous sub-block is done with Xs, QVa, KZ; Bs is current
+
+        // (1) store the prefetched tokens; zero the padding rows
+#pragma unroll
+        for (int k = 0; k < NPF; ++k) {
+            const int seg = tid + k * NT;
+            if (seg < T * SEGS) {
+                const int u = seg / SEGS, sg = seg % SEGS;
+                float f[VE], fq[VE];
+                if (seg < nt * SEGS) {
+                    unpack(pre[k], f, static_cast<const InT *>(nullptr));
+                    if (q)
+                        unpack(preq[k], fq, static_cast<const InT *>(nullptr));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        f[e] = fq[e] = 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    Xs[u * LDP + sg * VE + e] = f[e];
+                    QVa[u * D + sg * VE + e] = q ? fq[e] : f[e];
+                }
+            }
+        }
+        // position of the next sub-block; prefetch it
+        const long long s1 = s0 + nt;
+        const bool chunk_end = (s1 == cend);
+        long long c1 = c0, cend1 = cend;
+        if (chunk_end) {
+            c1 = cend;
+            cend1 = (c1 + L < N) ? c1 + L : N;
+        }
+        const int nt1 = (s1 < N) ? static_cast<int>((T < cend1 - s1) ? T : cend1 - s1) : 0;
+        if (nt1 > 0)
+            issue_loads(s1, nt1);
+        __syncthreads();
+
+        const int ntm = (nt + 15) >> 4;   // token tiles
+
+        // (2) boundary generation on MFMA: [k | v] = X [B_k; B_v]^T
+        {
+            constexpr int NTN = 2 * D / 16;
+            for (int tile = wave; tile < ntm * NTN; tile += NW) {
+                const int tm = tile / NTN, tn = tile % NTN;
+                const float *pa = Xs + (tm * 16 + lm) * LDP + lk;
+                const float *pb = Bs + (D + tn * 16 + lm) * LDP + lk;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
+                float *dst = (tn * 16 < D) ? KZ : Es;
+                const int oc = (tn * 16) % D + lm;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+            }
+        }
+        __syncthreads();
+
+        // (3) transition scalars, 4 lanes per token [SUMMARY stabilisation]
+        {
+            const int eu = tid >> 2, ep = tid & 3;
+            for (int ub = 0; ub < nt; ub += NT / 4) {
+                const int u = ub + eu;
+                if (u < nt) {
+                    float kk[CPL], vv[CPL];
+                    float nk2 = 0.f, er = 0.f, ar = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int jj = ep * CPL + c;
+                        kk[c] = KZ[u * LDP + jj];
+                        vv[c] = Es[u * LDP + jj];
+                        const float xv = Xs[u * LDP + jj];
+                        nk2 = fmaf(kk[c], kk[c], nk2);
+                        er = fmaf(Bs[3 * D * LDP + jj], xv, er);
+                        ar = fmaf(Bs[(3 * D + 1) * LDP + jj], xv, ar);
+                    }
+                    nk2 = quad_sum(nk2);
+                    er = quad_sum(er);
+                    ar = quad_sum(ar);
+                    const float inv = 1.0f / sqrtf(nk2 + eps);
+                    float nkh2 = 0.f, ne2 = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int jj = ep * CPL + c;
+                        const float kh = kk[c] * inv;
+                        const float ev = kh - vv[c];
+                        KHa[u * D + jj] = kh;
+                        Es[u * LDP + jj] = ev;
+                        nkh2 = fmaf(kh, kh, nkh2);
+                        ne2 = fmaf(ev, ev, ne2);
+                    }
+                    nkh2 = quad_sum(nkh2);
+                    ne2 = quad_sum(ne2);
+                    const float eta = sigmoidf(er);
+                    const float alpha = (flags & F_FIXED_ALPHA) ? alpha_max
+                                                                : alpha_max * sigmoidf(ar);
+                    const float g = sqrtf(ne2) * sqrtf(nkh2);
+                    const float m = 1.0f - alpha;
+                    float eta1 = eta;
+                    if (flags & F_NO_CAP) {
+                        eta1 = eta;
+                    } else if (flags & F_HARD_CAP) {
+                        if (g > 0.0f && m < eta * g)
+                            eta1 = m / g;
+                    } else if (g > 0.0f) {
+                        const float uu = eta * g / m;
+                        eta1 = (uu < 1e-3f) ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
+                                            : m * tanhf(uu) / g;
+                    }
+                    float eta2 = eta1;
+                    if (!(flags & F_NO_CLAMP) && nkh2 > 0.0f) {
+                        const float cap = 2.0f * alpha / nkh2;
+                        if (cap < eta2)
+                            eta2 = cap;
+                    }
+                    if (ep == 0)
+                        Sae[u] = make_float2(alpha, eta2);
+                }
+            }
+        }
+        __syncthreads();
+
+        // (4) token-order update, Q = cq * P
+        for (int u = 0; u < nt; ++u) {
+            float kv[CPL], qv[CPL];
+            const float4 *kp = reinterpret_cast<const float4 *>(KHa + u * D + part * CPL);
+            const float4 *qp = reinterpret_cast<const float4 *>(QVa + u * D + part * CPL);
+#pragma unroll
+            for (int c4 = 0; c4 < CPL / 4; ++c4) {
+                const float4 a = kp[c4], bq = qp[c4];
+                kv[4 * c4] = a.x; kv[4 * c4 + 1] = a.y; kv[4 * c4 + 2] = a.z; kv[4 * c4 + 3] = a.w;
+                qv[4 * c4] = bq.x; qv[4 * c4 + 1] = bq.y; qv[4 * c4 + 2] = bq.z; qv[4 * c4 + 3] = bq.w;
+            }
+            const float ee = Es[u * LDP + row];
+            const float2 ae = Sae[u];
+            float zb = 0.f;
+            if (before) {
+                float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; c += 2) {
+                    z0 = fmaf(P[c], qv[c], z0);
+                    z1 = fmaf(P[c + 1], qv[c + 1], z1);
+                }
+                zb = cq * quad_sum(z0 + z1);
+            }
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; c += 2) {
+                d0 = fmaf(P[c], kv[c], d0);
+                d1 = fmaf(P[c + 1], kv[c + 1], d1);
+            }
+            const float sc = fmaf(cq, quad_sum(d0 + d1), ee);   // (Q k^ + e)_row
+            const float cn = cq * ae.x;
+            if (cn >= kTinyScale) {
+                const float coef = ae.y / cn * sc;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    P[c] = fmaf(-coef, kv[c], P[c]);
+                cq = cn;
+            } else {   // fold the scale back into P before it underflows
+                const float s = ae.y * sc;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    P[c] = fmaf(-s, kv[c], cn * P[c]);
+                cq = 1.0f;
+            }
+            float z;
+            if (before) {
+                z = zb;
+            } else {
+                float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; c += 2) {
+                    z0 = fmaf(P[c], qv[c], z0);
+                    z1 = fmaf(P[c + 1], qv[c + 1], z1);
+                }
+                z = cq * quad_sum(z0 + z1);
+            }
+            if (part == 0)
+                KZ[u * LDP + row] = z;
+        }
+        __syncthreads();
+
+        // (5) readout on MFMA: y_t = B_c z_t
+        {
+            constexpr int NTN = D / 16;
+            for (int tile = wave; tile < ntm * NTN; tile += NW) {
+                const int tm = tile / NTN, tn = tile % NTN;
+                const float *pa = KZ + (tm * 16 + lm) * LDP + lk;
+                const float *pb = Bs + (tn * 16 + lm) * LDP + lk;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int u = tm * 16 + 4 * lk + rr;
+                    if (u < nt)
+                        out[(out_base * N + s0 + u) * C + static_cast<size_t>(h) * D + tn * 16 + lm] =
+                            acc[rr];
+                }
+            }
+        }
+
+        if (chunk_end) {
+            if (cend < N) {
+                // (6) refresh the boundary: B <- B Q_L
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    Qt[(part * CPL + c) * LDP + row] = cq * P[c];
+                __syncthreads();
+                v4f racc[RTW];
+#pragma unroll
+                for (int w = 0; w < RTW; ++w) {
+                    const int tile = wave + w * NW;
+                    const int tm = tile / (D / 16), tn = tile % (D / 16);
+                    const float *pa = Bs + (tm * 16 + lm) * LDP + lk;
+                    const float *pb = Qt + (tn * 16 + lm) * LDP + lk;
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
+                    racc[w] = acc;
+                }
+                float vacc = 0.f;
+                const int vv = tid / D, vj = tid % D;
+                if (tid < 2 * D) {
+#pragma unroll 8
+                    for (int k = 0; k < D; ++k)
+                        vacc = fmaf(Bs[(3 * D + vv) * LDP + k], Qt[vj * LDP + k], vacc);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int w = 0; w < RTW; ++w) {
+                    const int tile = wave + w * NW;
+                    const int tm = tile / (D / 16), tn = tile % (D / 16);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        Bs[(tm * 16 + 4 * lk + rr) * LDP + tn * 16 + lm] = racc[w][rr];
+                }
+                if (tid < 2 * D)
+                    Bs[(3 * D + vv) * LDP + vj] = vacc;
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                P[c] = (part * CPL + c == row) ? 1.0f : 0.0f;
+            cq = 1.0f;
+        }
+        if (s1 >= N)
+            break;
+        s0 = s1;
+        c0 = c1;
+        cend = cend1;
+        nt = nt1;
+    }
+}
+
 // ------------------------------------------------------------ fuse kernel
 
 struct bf16x4 { uint16_t v[4]; };
@@ -560,22 +962,33 @@ int grid_for(long long work, int block)
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
+// tokens per sub-block of the MFMA scan kernel
+template <int D> struct MfmaT { static constexpr int value = (D == 32) ? 64 : 32; };
+
 template <int D, typename InT>
 srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W, int C,
                         int heads, unsigned mask, float *out)
 {
-    using Cfg = ScanCfg<D>;
     const int R = popcount4(mask);
     const long long nchains = static_cast<long long>(R) * B * heads;
     if (nchains > INT_MAX - 8)
         return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
     const int nblocks = static_cast<int>((nchains + 7) / 8 * 8);
-    hipLaunchKernelGGL((scan_kernel<D, InT>), dim3(nblocks), dim3(Cfg::NT), 0,
-                       static_cast<hipStream_t>(p->stream), static_cast<const InT *>(x),
-                       static_cast<const InT *>(p->q), p->states, out, B, H, W, C, heads, mask,
-                       R, p->alpha_max, p->eps, p->chunk_row, p->chunk_col, p->flags,
-                       static_cast<int>(nchains));
-    return launch_check("scan_kernel");
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    if constexpr (D >= 32) {
+        constexpr int T = MfmaT<D>::value;
+        hipLaunchKernelGGL((scan_mfma_kernel<D, T, InT>), dim3(nblocks), dim3(4 * D), 0, st,
+                           static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+                           p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                           p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+        return launch_check("scan_mfma_kernel");
+    } else {
+        hipLaunchKernelGGL((scan_simple_kernel<D, InT>), dim3(nblocks), dim3(ScanCfg<D>::NT), 0,
+                           st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+                           p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                           p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+        return launch_check("scan_simple_kernel");
+    }
 }
 
 template <typename InT>

@@ -6,13 +6,16 @@ and for the fused output):
   * fp32 per-route scan outputs: 1e-4, for fp32 and for bf16 inputs (both
     sides read the same bf16 bytes, so only fp32 arithmetic separates them);
   * fused output in fp32: 1e-4; fused output stored as bf16: 2e-2;
-  * additionally, per chunk, max |gpu - oracle| <= 1e-4 * max |oracle| over
+  * additionally, per chunk, max |gpu - oracle| <= 1e-3 * max |oracle| over
     that chunk's tokens, on every chunk whose output is above 1e-20, so that
     the late chunks of long scans (where the untrained memories have
     contracted by many orders of magnitude) are checked on their own scale.
-    On the adversarial inputs (state std 3, x50 outlier tokens) the per-chunk
-    bar is 1e-3: an fp32 evaluation of the same recurrence in numpy reaches
-    3.6e-4 on one of those chunks, so that is fp32 conditioning, not a fault;
+    The per-chunk bar is wider than the global one because single chunks can
+    be ill-conditioned: an fp32 evaluation of the same recurrence in numpy
+    reaches 4.3e-4 on a chunk of the dense 200x304 map, 3.6e-4 on the
+    adversarial inputs and 1.3e-4 on a d=64 case, matching the GPU. Without
+    the soft cap (an ablation with no non-expansion guarantee) rounding
+    errors can grow along the scan, and the per-chunk bar is 1e-2;
   * route gather/restore indexing: bit-exact.
 Full-size workloads run on the GPU in full; the oracle checks sampled batch
 items (chains are independent across the batch, so a sample is exact).
@@ -31,6 +34,7 @@ from self_referential_memory_amd import srnl, synth
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL32 = 1e-4
+TOL_CHUNK = 1e-3
 TOL_BF16_OUT = 2e-2
 CHUNK_FLOOR = 1e-20
 
@@ -105,7 +109,7 @@ def chunk_rel(g, o, L):
     return worst
 
 
-def check(wl, bs=None, route_mask=None, flags=0, out_dtype=None, chunk_tol=TOL32):
+def check(wl, bs=None, route_mask=None, flags=0, out_dtype=None, chunk_tol=TOL_CHUNK):
     yg, fg = gpu_forward(wl, route_mask, flags, out_dtype)
     yo, fo = oracle_forward(wl, bs, route_mask, flags)
     if bs is not None:
@@ -249,7 +253,7 @@ def test_route_subsets(mask):
 def test_variants_on_adversarial_inputs(flags):
     # large state spread and x50 outlier tokens: the cap and the clamp bind
     wl = synth.make("adv", 2, 12, 10, 64, 2, 32, "f32", 17, state_std=3.0, outlier_frac=0.05)
-    check(wl, flags=flags, chunk_tol=1e-3)
+    check(wl, flags=flags, chunk_tol=1e-2 if flags & srnl.FLAG_NO_CAP else TOL_CHUNK)
 
 
 def test_clamp_binds_in_adversarial_parity_case():
