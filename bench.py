@@ -58,19 +58,55 @@ def traffic_from_profile(launches_units: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def pmc_summary(fetch_csv: str, write_csv: str, command: str) -> None:
+    """Digest two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of this
+    script with --copy-probe) into profiles/scan_kernel_hier56_traffic.json:
+    per-dispatch counter averages, calibrated against the plain 1 GiB device
+    copy the probe runs (1 GiB read and 1 GiB written per dispatch)."""
+    import csv
+    import collections
+
+    def read(path, counter):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+    gib = float(1 << 30)
+    f_scale = gib / (pick(fetch, "copyBuffer") * 1024.0)
+    w_scale = gib / (pick(write, "copyBuffer") * 1024.0)
+    out = {"kernel_source_sha": src_sha(), "command": command,
+           "copy_probe": {"bytes_each_way": int(gib), "fetch_scale": f_scale,
+                          "write_scale": w_scale}}
+    for key, name in (("scan_mfma_kernel<32", "scan_kernel"), ("fuse_kernel", "fuse_kernel")):
+        fb = pick(fetch, key) * 1024.0 * f_scale
+        wb = pick(write, key) * 1024.0 * w_scale
+        out[name] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                     "hbm_bytes_per_launch": fb + wb}
+    out["hbm_bytes_per_launch"] = out["scan_kernel"]["hbm_bytes_per_launch"]
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=2)
+    print(json.dumps(out, indent=2))
+
+
 def cpu_baseline(wl, n_items: int):
     import numpy as np
     import oracle
+    n_items = min(n_items, wl.B)
     sample = wl.x[:n_items]
     t0 = time.perf_counter()
     y = oracle.scan(sample, wl.states, wl.heads, wl.d, 15, alpha_max=wl.alpha_max, eps=wl.eps)
     oracle.fuse(y, n_items, wl.H, wl.W, wl.C, 15, wl.scales)
     dt = time.perf_counter() - t0
     units = n_items * wl.H * wl.W * wl.heads
+    what = ("the whole batch" if n_items == wl.B else
+            f"batch items 0..{n_items - 1} of {wl.B}")
     return {"value": units / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch items 0..{n_items - 1} of {wl.B} (all 4 routes, {wl.heads} heads, "
-                      f"{wl.H}x{wl.W}), scan + fuse, single-threaded double precision, "
-                      f"{dt:.1f} s"}
+            "sample": f"{what} (all 4 routes, {wl.heads} heads, {wl.H}x{wl.W}), scan + fuse, "
+                      f"single-threaded double-precision oracle, {dt:.1f} s"}
 
 
 def main():
@@ -78,12 +114,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-items", type=int, default=16,
-                    help="batch items the CPU-baseline oracle runs on")
+    ap.add_argument("--cpu-items", type=int, default=64,
+                    help="batch items the CPU-baseline oracle runs on (64 = the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="digest two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the operator's chains are independent and would shard over batch, "

@@ -43,6 +43,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <type_traits>
 
 #include "srnl.h"
 
@@ -384,39 +385,47 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
 
 // ------------------------------------------------------------ scan kernel, d = 32, 64
 //
-// One workgroup of 4d threads per chain; T tokens per sub-block (a chunk is
+// One workgroup of LPR*d threads per chain (LPR lanes per row of Q: 8 for
+// d = 32, so that a chain spans four waves and each SIMD holds two waves,
+// which a single wave's VALU issue rate needs; 4 for d = 64); T tokens per
+// sub-block (a chunk is
 // processed in sub-blocks of at most T tokens: generation inside a chunk
 // reads only the fixed boundary states, so it may be split).
 //
 //   load      tokens of the next sub-block are prefetched into registers
 //             (16-byte loads along the route) while the current one computes
-//   generate  [k | v] = X B_[k|v]^T on MFMA (v_mfma_f32_16x16x4f32)
-//   epilogue  4 lanes per token: |k|^2, b_eta . x, b_alpha . x, k^, e, the
-//             soft cap and the spectral clamp (quad DPP reductions)
-//   update    4 lanes per row of Q = cq * P, d/4 columns per lane; the
-//             retention factors accumulate in the scalar cq so the write is
-//             one FMA per element: P <- P - (eta''/cq') (cq P k^ + e) k^T
+//   generate  [k | v] = X [B_k; B_v]^T on MFMA (v_mfma_f32_16x16x4f32)
+//   epilogue  NT/T lanes per token: |k|^2, b_eta . x, b_alpha . x, k^, e, the
+//             soft cap, the spectral clamp, and the key Gram scalar
+//             k^_{t-1} . k^_t (DPP group reductions)
+//   scales    one wave forms the running retention products c_t of the
+//             sub-block (prefix product over its tokens)
+//   update    LPR lanes per row of Q = c P, d/LPR columns per lane (below)
 //   readout   Y = Z B_c^T on MFMA, z_t = Q_t q_t
 //   refresh   B <- B Q_L on MFMA (the two vector memories on VALU)
 //
-// MFMA 16x16x4 f32 operand layout (lane l): A[l%16][l/16], B[l/16][l%16],
-// D[4(l/16)+r][l%16] in accumulator register r. Every operand is read from
-// an LDS array stored [m or n][k] with row stride d+2, which puts the 64
-// lanes of one read on distinct banks.
+// MFMA 16x16x4 f32 operand layout (lane l): A[l%16][k], B[k][l%16] with the
+// k index of instruction s taken as (l/16) * d/4 + s (any bijection onto the
+// reduction index gives the same sum), so each lane's operands for one tile
+// are d/4 consecutive floats, read with ds_read_b128; D[4(l/16)+r][l%16] in
+// accumulator register r. Operand arrays are stored [m or n][k] with row
+// stride d+4 floats (16-byte aligned rows, distinct banks per 8-lane phase).
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int D, int T> struct MCfg {
-    static constexpr int NT = 4 * D;               // threads: 4 lanes per row of Q
+template <int D, int LPR, int T> struct MCfg {
+    static constexpr int NT = LPR * D;             // threads: LPR lanes per row of Q
     static constexpr int NW = NT / 64;             // waves
     static constexpr int ROWS = 3 * D + 2;
-    static constexpr int LDP = D + 2;              // operand row stride
-    static constexpr int CPL = D / 4;              // Q columns per lane
+    static constexpr int LDP = D + 4;              // operand row stride
+    static constexpr int CPL = D / LPR;            // Q columns per lane
     static constexpr int KS = D / 4;               // MFMA K-steps over d
-    static constexpr int RT = (3 * D / 16) * (D / 16);  // refresh tiles (matrix rows)
-    static constexpr int RTW = RT / NW;            // refresh tiles per wave
-    static_assert(RT % NW == 0, "refresh tiles must split evenly over waves");
+    static constexpr int TP = T + 2;               // token rows incl. two prefetch pad rows
+    static constexpr int NTC = D / 16;             // 16-wide column tiles of d
     static_assert(T % 16 == 0, "T must be a multiple of 16");
+    static_assert(T <= 64, "one wave scans the sub-block's retention products");
+    static_assert(CPL % 4 == 0, "lanes hold whole float4s of a row");
+    static_assert(NW % NTC == 0 || NTC % NW == 0, "tile split over waves");
 };
 
 // 16-byte vector of input elements
@@ -441,28 +450,88 @@ __device__ __forceinline__ void unpack(const uint4 &w, float (&f)[8], const uint
 
 constexpr float kTinyScale = 8.673617379884035e-19f;   // 2^-60
 
-template <int D, int T, typename InT>
-__global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
+// Sum over an aligned quad with DPP adds (fused v_add_f32_dpp).
+__device__ __forceinline__ float quad_sum_dpp(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
+// Sum over an aligned group of G lanes (G = 2, 4 or 8) with DPP adds.
+template <int G> __device__ __forceinline__ float group_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)); // xor 1
+    if (G >= 4)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)); // xor 2
+    if (G >= 8)   // row_half_mirror: lane i <- lane 7-i within each group of 8
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+    return v;
+}
+
+// 32-bit form of route_cell (the host guarantees H * W < 2^31).
+__device__ __forceinline__ void route_cell32(int r, int H, int W, int N, int t, int &i, int &j)
+{
+    const unsigned s = static_cast<unsigned>((r & 1) ? (N - 1 - t) : t);
+    if (r < 2) {
+        i = static_cast<int>(s / static_cast<unsigned>(W));
+        j = static_cast<int>(s - static_cast<unsigned>(i) * W);
+    } else {
+        j = static_cast<int>(s / static_cast<unsigned>(H));
+        i = static_cast<int>(s - static_cast<unsigned>(j) * H);
+    }
+}
+
+// n consecutive floats from LDS (16-byte aligned) into registers
+template <int n> __device__ __forceinline__ void lds_load(const float *p, float (&r)[n])
+{
+    static_assert(n % 4 == 0, "");
+#pragma unroll
+    for (int k = 0; k < n / 4; ++k) {
+        const float4 v = reinterpret_cast<const float4 *>(p)[k];
+        r[4 * k] = v.x;
+        r[4 * k + 1] = v.y;
+        r[4 * k + 2] = v.z;
+        r[4 * k + 3] = v.w;
+    }
+}
+
+// Per-token operands of the token loop for one lane: its CPL columns of k^
+// and q, e at its row, and the token's scalars.
+template <int CPL> struct TokOps {
+    float k[CPL];
+    float q[CPL];
+    float e;
+    float4 s;
+};
+
+template <int D, int LPR, int T, bool BEFORE, typename InT>
+__global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
     float eps, int chunk_row, int chunk_col, unsigned flags, int nchains)
 {
-    using Cfg = MCfg<D, T>;
+    using Cfg = MCfg<D, LPR, T>;
     constexpr int NT = Cfg::NT, NW = Cfg::NW, ROWS = Cfg::ROWS, LDP = Cfg::LDP,
-                  CPL = Cfg::CPL, KS = Cfg::KS, RTW = Cfg::RTW;
+                  CPL = Cfg::CPL, KS = Cfg::KS, TP = Cfg::TP, NTC = Cfg::NTC;
     constexpr int VE = InVec<InT>::VE;
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
     constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
+    constexpr int RT = (3 * D / 16) * NTC;             // refresh tiles (matrix memories)
+    static_assert(RT % NW == 0, "refresh tiles split evenly over waves");
+    constexpr int RTW = RT / NW;                       // refresh tiles per wave
 
     __shared__ __align__(16) float Bs[ROWS * LDP];     // boundary rows M_c, M_k, M_v, m_eta, m_alpha
     __shared__ __align__(16) float Xs[T * LDP];        // x_t (MFMA operand)
-    __shared__ __align__(16) float QVa[T * D];         // q_t (token loop)
     __shared__ __align__(16) float KZ[T * LDP];        // k (generation), then z_t (readout)
-    __shared__ __align__(16) float Es[T * LDP];        // v, then e = k^ - v
-    __shared__ __align__(16) float KHa[T * D];         // k^ (token loop)
-    __shared__ __align__(16) float2 Sae[T];            // (alpha_t, eta''_t)
+    __shared__ __align__(16) float Es[TP * LDP];       // v, then e = k^ - v
+    __shared__ __align__(16) float QVa[TP * D];        // q_t (token loop)
+    __shared__ __align__(16) float KHa[TP * D];        // k^_t (token loop)
+    __shared__ __align__(16) float4 Sx[TP];            // alpha_t, eta''_t, k^_{t-1} . k^_t, -
+    __shared__ __align__(16) float4 Sy[TP];            // c_{t-1}, eta''_t / c_t, c_t, k^_{t-1} . k^_t
     __shared__ __align__(16) float Qt[D * LDP];        // Q_L^T at the chunk end
+    __shared__ int s_fast;
 
     const int chain = xcd_remap(blockIdx.x, gridDim.x);
     if (chain >= nchains)
@@ -472,32 +541,42 @@ __global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
     const int h = bh % heads;
     const int b = bh / heads;
     const int r = nth_route(route_mask, slot);
-    const long long N = static_cast<long long>(H) * W;
-    long long L = (r < 2) ? (chunk_row > 0 ? chunk_row : W)
-                          : (chunk_col > 0 ? chunk_col : H);
+    const int N = H * W;
+    int L = (r < 2) ? (chunk_row > 0 ? chunk_row : W) : (chunk_col > 0 ? chunk_col : H);
     if (L > N)
         L = N;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int lm = lane & 15, lk = lane >> 4;        // MFMA operand row / k slot
-    const int row = tid >> 2, part = tid & 3;         // token-loop row of Q and column part
+    const int lm = lane & 15, lk = lane >> 4;        // MFMA operand row / k block
+    const int row = tid / LPR, part = tid % LPR;      // token-loop row of Q and column part
 
     const float *st = states + (static_cast<size_t>(r) * heads + h) * (ROWS * D);
     for (int idx = tid; idx < ROWS * D; idx += NT)
         Bs[(idx / D) * LDP + idx % D] = st[idx];
+    // the two pad rows are read (never used) by the prefetch of the last tokens
+    for (int idx = tid; idx < 2 * LDP; idx += NT)
+        Es[T * LDP + idx] = 0.f;
+    for (int idx = tid; idx < 2 * D; idx += NT) {
+        QVa[T * D + idx] = 0.f;
+        KHa[T * D + idx] = 0.f;
+    }
+    if (tid < 2) {
+        Sx[T + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+        Sy[T + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
-    const size_t xbase = static_cast<size_t>(b) * H * W * C + static_cast<size_t>(h) * D;
+    const size_t xbase = static_cast<size_t>(b) * N * C + static_cast<size_t>(h) * D;
     uint4 pre[NPF], preq[NPF];
-    auto issue_loads = [&](long long s, int n) {
+    auto issue_loads = [&](int s, int n) {
 #pragma unroll
         for (int k = 0; k < NPF; ++k) {
             const int seg = tid + k * NT;
             if (seg < n * SEGS) {
                 const int u = seg / SEGS, sg = seg % SEGS;
                 int i, j;
-                route_cell(r, H, W, N, s + u, i, j);
-                const size_t off = xbase + (static_cast<size_t>(i) * W + j) * C + sg * VE;
+                route_cell32(r, H, W, N, s + u, i, j);
+                const size_t off = xbase + static_cast<size_t>(i * W + j) * C + sg * VE;
                 pre[k] = *reinterpret_cast<const uint4 *>(x + off);
                 if (q)
                     preq[k] = *reinterpret_cast<const uint4 *>(q + off);
@@ -511,19 +590,18 @@ __global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
         P[c] = (part * CPL + c == row) ? 1.0f : 0.0f;
     float cq = 1.0f;
 
-    const size_t out_base = static_cast<size_t>(slot) * B + b;
-    const bool before = (flags & F_READ_BEFORE) != 0;
+    const size_t out_row0 = (static_cast<size_t>(slot) * B + b) * N;
 
-    long long c0 = 0;
-    long long cend = (L < N) ? L : N;
-    long long s0 = 0;
-    int nt = static_cast<int>((T < cend) ? T : cend);
+    int c0 = 0;
+    int cend = L;
+    int s0 = 0;
+    int nt = (T < cend) ? T : cend;
     issue_loads(s0, nt);
 
     while (true) {
         __syncthreads();   // previous sub-block is done with Xs, QVa, KZ; Bs is current
 
-        // (1) store the prefetched tokens; zero the padding rows
+        // (1) store the prefetched tokens (zero rows past nt)
 #pragma unroll
         for (int k = 0; k < NPF; ++k) {
             const int seg = tid + k * NT;
@@ -539,197 +617,289 @@ __global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
                     for (int e = 0; e < VE; ++e)
                         f[e] = fq[e] = 0.0f;
                 }
+                float4 *xd = reinterpret_cast<float4 *>(Xs + u * LDP + sg * VE);
+                float4 *qd = reinterpret_cast<float4 *>(QVa + u * D + sg * VE);
 #pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    Xs[u * LDP + sg * VE + e] = f[e];
-                    QVa[u * D + sg * VE + e] = q ? fq[e] : f[e];
+                for (int e = 0; e < VE / 4; ++e) {
+                    xd[e] = make_float4(f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
+                    qd[e] = q ? make_float4(fq[4 * e], fq[4 * e + 1], fq[4 * e + 2], fq[4 * e + 3])
+                              : make_float4(f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
                 }
             }
         }
         // position of the next sub-block; prefetch it
-        const long long s1 = s0 + nt;
+        const int s1 = s0 + nt;
         const bool chunk_end = (s1 == cend);
-        long long c1 = c0, cend1 = cend;
+        int c1 = c0, cend1 = cend;
         if (chunk_end) {
             c1 = cend;
-            cend1 = (c1 + L < N) ? c1 + L : N;
+            cend1 = (c1 < N - L) ? c1 + L : N;
         }
-        const int nt1 = (s1 < N) ? static_cast<int>((T < cend1 - s1) ? T : cend1 - s1) : 0;
+        const int nt1 = (s1 < N) ? ((T < cend1 - s1) ? T : cend1 - s1) : 0;
         if (nt1 > 0)
             issue_loads(s1, nt1);
         __syncthreads();
 
         const int ntm = (nt + 15) >> 4;   // token tiles
 
-        // (2) boundary generation on MFMA: [k | v] = X [B_k; B_v]^T
+        // (2) boundary generation on MFMA: [k | v] = X [B_k; B_v]^T; wave w
+        //     produces the 16-wide output tiles tn = w, w + NW, ...
         {
-            constexpr int NTN = 2 * D / 16;
-            for (int tile = wave; tile < ntm * NTN; tile += NW) {
-                const int tm = tile / NTN, tn = tile % NTN;
-                const float *pa = Xs + (tm * 16 + lm) * LDP + lk;
-                const float *pb = Bs + (D + tn * 16 + lm) * LDP + lk;
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
+            for (int tn = wave; tn < 2 * NTC; tn += NW) {
+                float bg[KS];
+                lds_load(Bs + (D + tn * 16 + lm) * LDP + lk * KS, bg);
+                float *dst = (tn < NTC) ? KZ : Es;
+                const int oc = (tn % NTC) * 16 + lm;
+                for (int tm = 0; tm < ntm; ++tm) {
+                    float a[KS];
+                    lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
-                float *dst = (tn * 16 < D) ? KZ : Es;
-                const int oc = (tn * 16) % D + lm;
+                    for (int s = 0; s < KS; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bg[s], acc, 0, 0, 0);
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
-            }
-        }
-        __syncthreads();
-
-        // (3) transition scalars, 4 lanes per token [SUMMARY stabilisation]
-        {
-            const int eu = tid >> 2, ep = tid & 3;
-            for (int ub = 0; ub < nt; ub += NT / 4) {
-                const int u = ub + eu;
-                if (u < nt) {
-                    float kk[CPL], vv[CPL];
-                    float nk2 = 0.f, er = 0.f, ar = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        const int jj = ep * CPL + c;
-                        kk[c] = KZ[u * LDP + jj];
-                        vv[c] = Es[u * LDP + jj];
-                        const float xv = Xs[u * LDP + jj];
-                        nk2 = fmaf(kk[c], kk[c], nk2);
-                        er = fmaf(Bs[3 * D * LDP + jj], xv, er);
-                        ar = fmaf(Bs[(3 * D + 1) * LDP + jj], xv, ar);
-                    }
-                    nk2 = quad_sum(nk2);
-                    er = quad_sum(er);
-                    ar = quad_sum(ar);
-                    const float inv = 1.0f / sqrtf(nk2 + eps);
-                    float nkh2 = 0.f, ne2 = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        const int jj = ep * CPL + c;
-                        const float kh = kk[c] * inv;
-                        const float ev = kh - vv[c];
-                        KHa[u * D + jj] = kh;
-                        Es[u * LDP + jj] = ev;
-                        nkh2 = fmaf(kh, kh, nkh2);
-                        ne2 = fmaf(ev, ev, ne2);
-                    }
-                    nkh2 = quad_sum(nkh2);
-                    ne2 = quad_sum(ne2);
-                    const float eta = sigmoidf(er);
-                    const float alpha = (flags & F_FIXED_ALPHA) ? alpha_max
-                                                                : alpha_max * sigmoidf(ar);
-                    const float g = sqrtf(ne2) * sqrtf(nkh2);
-                    const float m = 1.0f - alpha;
-                    float eta1 = eta;
-                    if (flags & F_NO_CAP) {
-                        eta1 = eta;
-                    } else if (flags & F_HARD_CAP) {
-                        if (g > 0.0f && m < eta * g)
-                            eta1 = m / g;
-                    } else if (g > 0.0f) {
-                        const float uu = eta * g / m;
-                        eta1 = (uu < 1e-3f) ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
-                                            : m * tanhf(uu) / g;
-                    }
-                    float eta2 = eta1;
-                    if (!(flags & F_NO_CLAMP) && nkh2 > 0.0f) {
-                        const float cap = 2.0f * alpha / nkh2;
-                        if (cap < eta2)
-                            eta2 = cap;
-                    }
-                    if (ep == 0)
-                        Sae[u] = make_float2(alpha, eta2);
+                    for (int rr = 0; rr < 4; ++rr)
+                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
                 }
             }
         }
         __syncthreads();
 
-        // (4) token-order update, Q = cq * P
-        for (int u = 0; u < nt; ++u) {
-            float kv[CPL], qv[CPL];
-            const float4 *kp = reinterpret_cast<const float4 *>(KHa + u * D + part * CPL);
-            const float4 *qp = reinterpret_cast<const float4 *>(QVa + u * D + part * CPL);
+        // (3) transition scalars, EPL lanes per token [SUMMARY stabilisation];
+        //     also the key Gram scalar k^_{t-1} . k^_t used by the token loop
+        {
+            constexpr int EPL = NT / T;
+            constexpr int ECPL = D / EPL;
+            static_assert(EPL * T == NT && (EPL == 2 || EPL == 4 || EPL == 8), "epilogue lanes");
+            const int u = tid / EPL, ep = tid % EPL;
+            if (u < nt) {
+                const int up = (u > 0) ? u - 1 : 0;
+                float kk[ECPL], vv[ECPL], xv[ECPL], kp[ECPL], be[ECPL], ba[ECPL];
+                lds_load(KZ + u * LDP + ep * ECPL, kk);
+                lds_load(Es + u * LDP + ep * ECPL, vv);
+                lds_load(Xs + u * LDP + ep * ECPL, xv);
+                lds_load(KZ + up * LDP + ep * ECPL, kp);
+                lds_load(Bs + 3 * D * LDP + ep * ECPL, be);
+                lds_load(Bs + (3 * D + 1) * LDP + ep * ECPL, ba);
+                float nk2 = 0.f, er = 0.f, ar = 0.f, np2 = 0.f, kdot = 0.f;
 #pragma unroll
-            for (int c4 = 0; c4 < CPL / 4; ++c4) {
-                const float4 a = kp[c4], bq = qp[c4];
-                kv[4 * c4] = a.x; kv[4 * c4 + 1] = a.y; kv[4 * c4 + 2] = a.z; kv[4 * c4 + 3] = a.w;
-                qv[4 * c4] = bq.x; qv[4 * c4 + 1] = bq.y; qv[4 * c4 + 2] = bq.z; qv[4 * c4 + 3] = bq.w;
-            }
-            const float ee = Es[u * LDP + row];
-            const float2 ae = Sae[u];
-            float zb = 0.f;
-            if (before) {
-                float z0 = 0.f, z1 = 0.f;
-#pragma unroll
-                for (int c = 0; c < CPL; c += 2) {
-                    z0 = fmaf(P[c], qv[c], z0);
-                    z1 = fmaf(P[c + 1], qv[c + 1], z1);
+                for (int c = 0; c < ECPL; ++c) {
+                    nk2 = fmaf(kk[c], kk[c], nk2);
+                    np2 = fmaf(kp[c], kp[c], np2);
+                    kdot = fmaf(kp[c], kk[c], kdot);
+                    er = fmaf(be[c], xv[c], er);
+                    ar = fmaf(ba[c], xv[c], ar);
                 }
-                zb = cq * quad_sum(z0 + z1);
-            }
-            float d0 = 0.f, d1 = 0.f;
+                nk2 = group_sum<EPL>(nk2);
+                np2 = group_sum<EPL>(np2);
+                kdot = group_sum<EPL>(kdot);
+                er = group_sum<EPL>(er);
+                ar = group_sum<EPL>(ar);
+                const float inv = __builtin_amdgcn_rsqf(nk2 + eps);
+                const float gram = kdot * inv * __builtin_amdgcn_rsqf(np2 + eps);
+                float nkh2 = 0.f, ne2 = 0.f;
+                float khv[ECPL], evv[ECPL];
 #pragma unroll
-            for (int c = 0; c < CPL; c += 2) {
-                d0 = fmaf(P[c], kv[c], d0);
-                d1 = fmaf(P[c + 1], kv[c + 1], d1);
+                for (int c = 0; c < ECPL; ++c) {
+                    khv[c] = kk[c] * inv;
+                    evv[c] = khv[c] - vv[c];
+                    nkh2 = fmaf(khv[c], khv[c], nkh2);
+                    ne2 = fmaf(evv[c], evv[c], ne2);
+                }
+                float4 *kd = reinterpret_cast<float4 *>(KHa + u * D + ep * ECPL);
+                float4 *ed = reinterpret_cast<float4 *>(Es + u * LDP + ep * ECPL);
+#pragma unroll
+                for (int c4 = 0; c4 < ECPL / 4; ++c4) {
+                    kd[c4] = make_float4(khv[4 * c4], khv[4 * c4 + 1], khv[4 * c4 + 2], khv[4 * c4 + 3]);
+                    ed[c4] = make_float4(evv[4 * c4], evv[4 * c4 + 1], evv[4 * c4 + 2], evv[4 * c4 + 3]);
+                }
+                nkh2 = group_sum<EPL>(nkh2);
+                ne2 = group_sum<EPL>(ne2);
+                const float eta = sigmoidf(er);
+                const float alpha = (flags & F_FIXED_ALPHA) ? alpha_max
+                                                            : alpha_max * sigmoidf(ar);
+                const float g = sqrtf(ne2 * nkh2);
+                const float m = 1.0f - alpha;
+                float eta1 = eta;
+                if (flags & F_NO_CAP) {
+                    eta1 = eta;
+                } else if (flags & F_HARD_CAP) {
+                    if (g > 0.0f && m < eta * g)
+                        eta1 = m * __builtin_amdgcn_rcpf(g);
+                } else if (g > 0.0f) {
+                    const float uu = eta * g * __builtin_amdgcn_rcpf(m);
+                    eta1 = (uu < 1e-3f) ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
+                                        : m * tanhf(uu) * __builtin_amdgcn_rcpf(g);
+                }
+                float eta2 = eta1;
+                if (!(flags & F_NO_CLAMP) && nkh2 > 0.0f) {
+                    const float cap = 2.0f * alpha * __builtin_amdgcn_rcpf(nkh2);
+                    if (cap < eta2)
+                        eta2 = cap;
+                }
+                if (ep == 0)
+                    Sx[u] = make_float4(alpha, eta2, gram, 0.f);
             }
-            const float sc = fmaf(cq, quad_sum(d0 + d1), ee);   // (Q k^ + e)_row
-            const float cn = cq * ae.x;
-            if (cn >= kTinyScale) {
-                const float coef = ae.y / cn * sc;
+        }
+        __syncthreads();
+
+        // (3b) running retention products of the sub-block (wave 0, lane = token):
+        //      c_t = alpha_0 ... alpha_t, with the sub-block starting at scale 1.
+        //      If c stays above 2^-60 the token loop takes the fast form.
+        if (wave == 0) {
+            const float4 sx = Sx[(lane < nt) ? lane : 0];
+            float cprod = (lane < nt) ? sx.x : 1.0f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(cprod, off);
+                if (lane >= off)
+                    cprod *= o;
+            }
+            float cprev = __shfl_up(cprod, 1);
+            if (lane == 0)
+                cprev = 1.0f;
+            const float clast = __shfl(cprod, nt - 1);
+            if (lane < nt)
+                Sy[lane] = make_float4(cprev, sx.y * __builtin_amdgcn_rcpf(cprod), cprod, sx.z);
+            if (lane == 0)
+                s_fast = clast >= kTinyScale;
+        }
+        __syncthreads();
+
+        // (4) token-order update, LPR lanes per row of Q = cq P, CPL columns per
+        //     lane. Per token t, for this lane's row:
+        //       sc = (Q_{t-1} k^_t + e_t)_row,   w = (eta''_t / c_t) sc,
+        //       P_t = P_{t-1} - w k^_t^T         (Q_t = alpha_t Q_{t-1} - eta''_t sc k^_t^T)
+        //     The next token's dot needs no fresh reduction on the critical
+        //     path: P_t . k^_{t+1} = pre - w G_{t,t+1}, with pre = P_{t-1} . k^_{t+1}
+        //     reduced one token earlier and G from the epilogue. Operands are
+        //     prefetched two tokens ahead (three rotating register buffers).
+        //     Fast form: the sub-block starts at scale 1 and uses the
+        //     precomputed c_t. General form (a running product would fall
+        //     below 2^-60): the scale is tracked token by token and folded
+        //     into P before it underflows.
+        {
+            auto run = [&](auto fast_tag) {
+                constexpr bool FAST = decltype(fast_tag)::value;
+                if (FAST) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        P[c] *= cq;
+                    cq = 1.0f;
+                }
+                auto load_tok = [&](int u, TokOps<CPL> &o) {
+                    lds_load(KHa + u * D + part * CPL, o.k);
+                    lds_load(QVa + u * D + part * CPL, o.q);
+                    o.e = Es[u * LDP + row];
+                    o.s = FAST ? Sy[u] : Sx[u];
+                };
+                TokOps<CPL> t0, t1, t2;
+                load_tok(0, t0);
+                load_tok(1, t1);
+                float dk = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    P[c] = fmaf(-coef, kv[c], P[c]);
-                cq = cn;
-            } else {   // fold the scale back into P before it underflows
-                const float s = ae.y * sc;
+                    dk = fmaf(P[c], t0.k[c], dk);
+                dk = group_sum<LPR>(dk);
+                auto step = [&](int u, TokOps<CPL> &cur, TokOps<CPL> &nxt, TokOps<CPL> &nn) {
+                    load_tok(u + 2, nn);
+                    float p = 0.f, zb = 0.f;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    P[c] = fmaf(-s, kv[c], cn * P[c]);
-                cq = 1.0f;
-            }
-            float z;
-            if (before) {
-                z = zb;
-            } else {
-                float z0 = 0.f, z1 = 0.f;
+                    for (int c = 0; c < CPL; ++c) {
+                        p = fmaf(P[c], nxt.k[c], p);
+                        if (BEFORE)
+                            zb = fmaf(P[c], cur.q[c], zb);
+                    }
+                    const float pre = group_sum<LPR>(p);
+                    float z = 0.f, w, fold = 1.0f, gnext;
+                    if (FAST) {
+                        const float sc = fmaf(cur.s.x, dk, cur.e);
+                        w = cur.s.y * sc;
+                        if (BEFORE)
+                            z = cur.s.x * group_sum<LPR>(zb);
+                        gnext = nxt.s.w;
+                    } else {
+                        const float sc = fmaf(cq, dk, cur.e);
+                        const float cn = cq * cur.s.x;
+                        const bool small = cn < kTinyScale;
+                        const float cqn = small ? 1.0f : cn;
+                        fold = small ? cn : 1.0f;
+                        w = cur.s.y * __builtin_amdgcn_rcpf(cqn) * sc;
+                        if (BEFORE)
+                            z = cq * group_sum<LPR>(zb);
+                        if (small) {
 #pragma unroll
-                for (int c = 0; c < CPL; c += 2) {
-                    z0 = fmaf(P[c], qv[c], z0);
-                    z1 = fmaf(P[c + 1], qv[c + 1], z1);
+                            for (int c = 0; c < CPL; ++c)
+                                P[c] *= cn;
+                        }
+                        cq = cqn;
+                        gnext = nxt.s.z;
+                    }
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        P[c] = fmaf(-w, cur.k[c], P[c]);
+                    if (!BEFORE) {
+                        float zz = 0.f;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c)
+                            zz = fmaf(P[c], cur.q[c], zz);
+                        z = (FAST ? cur.s.z : cq) * group_sum<LPR>(zz);
+                    }
+                    KZ[u * LDP + row] = z;   // the LPR lanes of the row store the same value
+                    dk = fmaf(-w, gnext, fold * pre);
+                };
+                int u = 0;
+                for (; u + 2 < nt; u += 3) {
+                    step(u, t0, t1, t2);
+                    step(u + 1, t1, t2, t0);
+                    step(u + 2, t2, t0, t1);
                 }
-                z = cq * quad_sum(z0 + z1);
-            }
-            if (part == 0)
-                KZ[u * LDP + row] = z;
+                if (u < nt)
+                    step(u, t0, t1, t2);
+                if (u + 1 < nt)
+                    step(u + 1, t1, t2, t0);
+                if (FAST)
+                    cq = Sy[nt - 1].z;
+            };
+            if (s_fast)
+                run(std::true_type{});
+            else
+                run(std::false_type{});
         }
         __syncthreads();
 
-        // (5) readout on MFMA: y_t = B_c z_t
+        // (5) readout on MFMA: y_t = B_c z_t. With more waves than 16-wide
+        //     channel tiles, wave w takes the token tiles tm = w, w + NW, ... and
+        //     writes whole output rows of its head; otherwise wave w takes the
+        //     channel tiles tn = w, w + NW, ... for every token tile.
         {
-            constexpr int NTN = D / 16;
-            for (int tile = wave; tile < ntm * NTN; tile += NW) {
-                const int tm = tile / NTN, tn = tile % NTN;
-                const float *pa = KZ + (tm * 16 + lm) * LDP + lk;
-                const float *pb = Bs + (tn * 16 + lm) * LDP + lk;
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
+            constexpr bool BY_TOKENS = NW > NTC;
+            const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
+            const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
+            for (int tm = tm0; tm < ntm; tm += tms) {
+                float a[KS];
+                lds_load(KZ + (tm * 16 + lm) * LDP + lk * KS, a);
+                for (int tn = tn0; tn < NTC; tn += tns) {
+                    float br[KS];
+                    lds_load(Bs + (tn * 16 + lm) * LDP + lk * KS, br);
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
+                    for (int s = 0; s < KS; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], br[s], acc, 0, 0, 0);
+                    float *orow = out + (out_row0 + s0) * C + static_cast<size_t>(h) * D + tn * 16 + lm;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int u = tm * 16 + 4 * lk + rr;
-                    if (u < nt)
-                        out[(out_base * N + s0 + u) * C + static_cast<size_t>(h) * D + tn * 16 + lm] =
-                            acc[rr];
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int u0 = tm * 16 + 4 * lk + rr;
+                        if (u0 < nt)
+                            orow[static_cast<size_t>(u0) * C] = acc[rr];
+                    }
                 }
             }
         }
 
         if (chunk_end) {
             if (cend < N) {
-                // (6) refresh the boundary: B <- B Q_L
+                // (6) refresh the boundary: B <- B Q_L (tiles split over the waves)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     Qt[(part * CPL + c) * LDP + row] = cq * P[c];
@@ -738,27 +908,35 @@ __global__ __launch_bounds__(4 * D) void scan_mfma_kernel(
 #pragma unroll
                 for (int w = 0; w < RTW; ++w) {
                     const int tile = wave + w * NW;
-                    const int tm = tile / (D / 16), tn = tile % (D / 16);
-                    const float *pa = Bs + (tm * 16 + lm) * LDP + lk;
-                    const float *pb = Qt + (tn * 16 + lm) * LDP + lk;
+                    const int tm = tile / NTC, tn = tile % NTC;
+                    float a[KS], bq[KS];
+                    lds_load(Bs + (tm * 16 + lm) * LDP + lk * KS, a);
+                    lds_load(Qt + (tn * 16 + lm) * LDP + lk * KS, bq);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * s], pb[4 * s], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bq[s], acc, 0, 0, 0);
                     racc[w] = acc;
                 }
                 float vacc = 0.f;
                 const int vv = tid / D, vj = tid % D;
                 if (tid < 2 * D) {
-#pragma unroll 8
-                    for (int k = 0; k < D; ++k)
-                        vacc = fmaf(Bs[(3 * D + vv) * LDP + k], Qt[vj * LDP + k], vacc);
+                    const float4 *br4 = reinterpret_cast<const float4 *>(Bs + (3 * D + vv) * LDP);
+                    const float4 *q4 = reinterpret_cast<const float4 *>(Qt + vj * LDP);
+#pragma unroll
+                    for (int k = 0; k < D / 4; ++k) {
+                        const float4 bb = br4[k], qq = q4[k];
+                        vacc = fmaf(bb.x, qq.x, vacc);
+                        vacc = fmaf(bb.y, qq.y, vacc);
+                        vacc = fmaf(bb.z, qq.z, vacc);
+                        vacc = fmaf(bb.w, qq.w, vacc);
+                    }
                 }
                 __syncthreads();
 #pragma unroll
                 for (int w = 0; w < RTW; ++w) {
                     const int tile = wave + w * NW;
-                    const int tm = tile / (D / 16), tn = tile % (D / 16);
+                    const int tm = tile / NTC, tn = tile % NTC;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
                         Bs[(tm * 16 + 4 * lk + rr) * LDP + tn * 16 + lm] = racc[w][rr];
@@ -962,8 +1140,9 @@ int grid_for(long long work, int block)
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
-// tokens per sub-block of the MFMA scan kernel
+// tokens per sub-block and lanes per row of Q of the MFMA scan kernel
 template <int D> struct MfmaT { static constexpr int value = (D == 32) ? 64 : 32; };
+template <int D> struct MfmaLPR { static constexpr int value = (D == 32) ? 8 : 4; };
 
 template <int D, typename InT>
 srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W, int C,
@@ -977,10 +1156,17 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
     hipStream_t st = static_cast<hipStream_t>(p->stream);
     if constexpr (D >= 32) {
         constexpr int T = MfmaT<D>::value;
-        hipLaunchKernelGGL((scan_mfma_kernel<D, T, InT>), dim3(nblocks), dim3(4 * D), 0, st,
-                           static_cast<const InT *>(x), static_cast<const InT *>(p->q),
-                           p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
-                           p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+        constexpr int LPR = MfmaLPR<D>::value;
+        if (p->flags & F_READ_BEFORE)
+            hipLaunchKernelGGL((scan_mfma_kernel<D, LPR, T, true, InT>), dim3(nblocks), dim3(LPR * D), 0,
+                               st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+                               p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                               p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+        else
+            hipLaunchKernelGGL((scan_mfma_kernel<D, LPR, T, false, InT>), dim3(nblocks), dim3(LPR * D), 0,
+                               st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+                               p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                               p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
         return launch_check("scan_mfma_kernel");
     } else {
         hipLaunchKernelGGL((scan_simple_kernel<D, InT>), dim3(nblocks), dim3(ScanCfg<D>::NT), 0,

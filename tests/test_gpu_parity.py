@@ -13,9 +13,7 @@ and for the fused output):
     The per-chunk bar is wider than the global one because single chunks can
     be ill-conditioned: an fp32 evaluation of the same recurrence in numpy
     reaches 4.3e-4 on a chunk of the dense 200x304 map, 3.6e-4 on the
-    adversarial inputs and 1.3e-4 on a d=64 case, matching the GPU. Without
-    the soft cap (an ablation with no non-expansion guarantee) rounding
-    errors can grow along the scan, and the per-chunk bar is 1e-2;
+    adversarial inputs and 1.3e-4 on a d=64 case, matching the GPU;
   * route gather/restore indexing: bit-exact.
 Full-size workloads run on the GPU in full; the oracle checks sampled batch
 items (chains are independent across the batch, so a sample is exact).
@@ -251,9 +249,15 @@ def test_route_subsets(mask):
                                    srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE,
                                    srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP])
 def test_variants_on_adversarial_inputs(flags):
-    # large state spread and x50 outlier tokens: the cap and the clamp bind
-    wl = synth.make("adv", 2, 12, 10, 64, 2, 32, "f32", 17, state_std=3.0, outlier_frac=0.05)
-    check(wl, flags=flags, chunk_tol=1e-2 if flags & srnl.FLAG_NO_CAP else TOL_CHUNK)
+    # large state spread and x50 outlier tokens: the cap and the clamp bind.
+    # Without the cap these inputs are expansive (memory norms grow ~6e15x
+    # over the boundary's), so rounding differences grow without bound and
+    # the no-cap ablation is checked on milder states (std 0.3, growth 3.5x).
+    if flags & srnl.FLAG_NO_CAP:
+        wl = synth.make("nocap", 2, 12, 10, 64, 2, 32, "f32", 17, state_std=0.3)
+    else:
+        wl = synth.make("adv", 2, 12, 10, 64, 2, 32, "f32", 17, state_std=3.0, outlier_frac=0.05)
+    check(wl, flags=flags)
 
 
 def test_clamp_binds_in_adversarial_parity_case():
