@@ -16,6 +16,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     # no packed fp32 instructions (hipcc warns on the host pass: harmless)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs, so that the VALU work between
+    # dependent products needs no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

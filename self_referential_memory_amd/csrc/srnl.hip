@@ -385,48 +385,135 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
 
 // ------------------------------------------------------------ scan kernel, d = 32, 64
 //
-// One workgroup of LPR*d threads per chain (LPR lanes per row of Q: 8 for
-// d = 32, so that a chain spans four waves and each SIMD holds two waves,
-// which a single wave's VALU issue rate needs; 4 for d = 64); T tokens per
-// sub-block (a chunk is
-// processed in sub-blocks of at most T tokens: generation inside a chunk
-// reads only the fixed boundary states, so it may be split).
+// One workgroup of NW waves per chain; T tokens per sub-block (a chunk is
+// processed in sub-blocks of at most T tokens: generation inside a chunk reads
+// only the fixed boundary states, so it may be split), and each sub-block in
+// windows of 16 tokens.
 //
 //   load      tokens of the next sub-block are prefetched into registers
 //             (16-byte loads along the route) while the current one computes
 //   generate  [k | v] = X [B_k; B_v]^T on MFMA (v_mfma_f32_16x16x4f32)
 //   epilogue  NT/T lanes per token: |k|^2, b_eta . x, b_alpha . x, k^, e, the
-//             soft cap, the spectral clamp, and the key Gram scalar
-//             k^_{t-1} . k^_t (DPP group reductions)
-//   scales    one wave forms the running retention products c_t of the
-//             sub-block (prefix product over its tokens)
-//   update    LPR lanes per row of Q = c P, d/LPR columns per lane (below)
+//             soft cap and the spectral clamp (DPP group reductions)
+//   windows   one wave per 16-token window: key/key and query/key Gram
+//             matrices on MFMA, retention products, and the window's
+//             triangular system (below)
+//   update    the token-order update of a window as dense products on MFMA;
+//             the rows of Q are independent, so wave w owns rows
+//             16w .. 16w+15 of Q (held transposed, in MFMA accumulators) and
+//             the waves never exchange data inside a sub-block
 //   readout   Y = Z B_c^T on MFMA, z_t = Q_t q_t
 //   refresh   B <- B Q_L on MFMA (the two vector memories on VALU)
 //
-// MFMA 16x16x4 f32 operand layout (lane l): A[l%16][k], B[k][l%16] with the
-// k index of instruction s taken as (l/16) * d/4 + s (any bijection onto the
-// reduction index gives the same sum), so each lane's operands for one tile
-// are d/4 consecutive floats, read with ds_read_b128; D[4(l/16)+r][l%16] in
-// accumulator register r. Operand arrays are stored [m or n][k] with row
-// stride d+4 floats (16-byte aligned rows, distinct banks per 8-lane phase).
+// Windowed form of the update. Write the update of one token as
+// Q_t = alpha_t Q_{t-1} + u_t k^_t^T with u_t = -eta''_t (Q_{t-1} k^_t + e_t).
+// Over a window that starts from Q_0, with local products
+// G_t = alpha_0 ... alpha_t (G_{-1} = 1) and R[t][s] = alpha_{s+1} ... alpha_t
+// (R[t][t] = 1):
+//   Q_t = G_t Q_0 + sum_{s<=t} R[t][s] u_s k^_s^T,
+// so the u_s solve the unit lower-triangular system
+//   u_t + sum_{s<t} L[t][s] u_s = -eta''_t (G_{t-1} Q_0 k^_t + e_t),
+//   L[t][s] = eta''_t R[t-1][s] (k^_s . k^_t),
+// i.e. U = T' (A + E) with T' = (I + L)^-1 diag(-eta''), A[t] = G_{t-1} Q_0 k^_t.
+// Then z_t = Q_t q_t = G_t Q_0 q_t + sum_{s<=t} R[t][s] (k^_s . q_t) u_s and
+// Q_16 = G_15 Q_0 + sum_s R[15][s] u_s k^_s^T. Every product is exact
+// algebra of the token-order recurrence; only the summation order differs.
+// Ratios of retention products are never formed (R is built from products of
+// the alphas themselves), so tiny retentions need no rescaling. Padding
+// tokens of a short window carry alpha = 1, eta'' = 0, k^ = e = q = 0 and
+// change nothing.
+//
+// MFMA 16x16x4 f32 operand layout (lane l, lm = l % 16, lk = l / 16):
+// A[lm][k], B[k][lm], D[4 lk + r][lm] in accumulator register r. Over the four
+// instructions r = 0..3 of one 16-wide block of the reduction index, lane l
+// supplies reduction index 4 lk + r, so an accumulator tile can serve directly
+// as the B operand of a product that contracts over its row index, and a lane's
+// A or B operands from a [row][reduction] array are one 16-byte read.
+// [token][channel] arrays have row stride d + 4 floats, [channel][token]
+// arrays T + 4, the per-window 16 x 16 tables 20: 16-byte aligned rows whose
+// 16-byte reads by 8 consecutive lanes hit distinct banks.
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int D, int LPR, int T> struct MCfg {
-    static constexpr int NT = LPR * D;             // threads: LPR lanes per row of Q
-    static constexpr int NW = NT / 64;             // waves
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// c += A B over one 16-wide block of the reduction index (4 instructions)
+__device__ __forceinline__ v4f mfma16(const float4 &a, const float4 &b, v4f c)
+{
+    c = mfma4(a.x, b.x, c);
+    c = mfma4(a.y, b.y, c);
+    c = mfma4(a.z, b.z, c);
+    c = mfma4(a.w, b.w, c);
+    return c;
+}
+__device__ __forceinline__ v4f mfma16(const float4 &a, const v4f &b, v4f c)
+{
+    c = mfma4(a.x, b[0], c);
+    c = mfma4(a.y, b[1], c);
+    c = mfma4(a.z, b[2], c);
+    c = mfma4(a.w, b[3], c);
+    return c;
+}
+
+template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
+    static constexpr int NW = NW_;                 // waves per chain
+    static constexpr int NT = NW * 64;             // threads
     static constexpr int ROWS = 3 * D + 2;
-    static constexpr int LDP = D + 4;              // operand row stride
-    static constexpr int CPL = D / LPR;            // Q columns per lane
+    static constexpr int LDP = D + 4;              // [token][channel] row stride
     static constexpr int KS = D / 4;               // MFMA K-steps over d
-    static constexpr int TP = T + 2;               // token rows incl. two prefetch pad rows
     static constexpr int NTC = D / 16;             // 16-wide column tiles of d
-    static_assert(T % 16 == 0, "T must be a multiple of 16");
-    static_assert(T <= 64, "one wave scans the sub-block's retention products");
-    static_assert(CPL % 4 == 0, "lanes hold whole float4s of a row");
-    static_assert(NW % NTC == 0 || NTC % NW == 0, "tile split over waves");
+    static constexpr int NWIN = T / 16;            // windows per sub-block
+    static constexpr int ETS = T + 4;              // [channel][token] row stride
+    static constexpr int WS = 20;                  // row stride of the per-window N tables
+    static constexpr int JS = (NW >= 2 * NTC) ? 2 : 1;   // waves sharing 16 rows of Q
+    static constexpr int NJ = NTC / JS;            // 16-column tiles of Q per wave
+    static constexpr int CW = NTC * JS;            // waves in the token-order update
+    static_assert(T % 16 == 0 && T <= 64, "sub-block of whole windows");
+    static_assert(NW >= NTC, "one wave per 16 rows of Q");
+    static_assert(NTC % JS == 0 && (JS == 1 || CW == NW), "column split over whole tiles, all waves");
+    static_assert(NT >= 2 * D, "vector-memory refresh: one thread per output");
+
+    // LDS pool (floats). Arrays that are dead in a phase lend their space:
+    // the k rows (dead after the epilogue, until the update writes z) hold
+    // the windows' L^T tables; the v rows (dead after the epilogue) hold the
+    // N and T' tables, and at a chunk end Q_L^T when it fits.
+    static constexpr int SZ_TOK = T * LDP;
+    static constexpr int SZ_LC = NWIN * 256;
+    static constexpr int SZ_NN = NWIN * 16 * WS;
+    static constexpr int SZ_TP = NWIN * 256;
+    static constexpr int SZ_QT = D * LDP;
+    static_assert(SZ_LC <= SZ_TOK && SZ_NN + SZ_TP <= SZ_TOK, "window tables fit");
+    static constexpr bool QT_IN_ES = SZ_QT <= SZ_TOK;
+    static constexpr int O_BS = 0;
+    static constexpr int O_XS = O_BS + ROWS * LDP;
+    static constexpr int O_KZ = O_XS + SZ_TOK;
+    static constexpr int O_ES = O_KZ + SZ_TOK;
+    static constexpr int O_KH = O_ES + SZ_TOK;
+    static constexpr int O_ET = O_KH + SZ_TOK;
+    static constexpr int O_AL = O_ET + D * ETS;
+    static constexpr int O_EH = O_AL + T;
+    static constexpr int O_GA = O_EH + T;
+    static constexpr int O_GZ = O_GA + T;
+    static constexpr int O_RB = O_GZ + T;
+    static constexpr int O_WG = O_RB + T;
+    static constexpr int O_PI = O_WG + 4;
+    static constexpr int O_XB = O_PI + T;
+    static constexpr int SZ_XB = (JS == 2) ? 2 * NTC * 768 : 0;
+    static constexpr int O_QV = O_XB + SZ_XB;
+    static constexpr int O_QT = QT_IN_ES ? O_ES : O_QV + (HAS_Q ? SZ_TOK : 0);
+    static constexpr int POOL = (QT_IN_ES ? O_QV : O_QT + SZ_QT) + (HAS_Q ? SZ_TOK : 0);
 };
+
+// Index of T'[s][t] in a window's 16 x 16 table: rows of 16 floats, the four
+// 16-byte groups of a row rotated by (s >> 1) & 3 so that the 16-byte reads
+// of 8 consecutive rows hit distinct banks.
+__device__ __forceinline__ int tp_index(int s, int t)
+{
+    return s * 16 + ((((t >> 2) ^ (s >> 1)) & 3) << 2) + (t & 3);
+}
 
 // 16-byte vector of input elements
 template <typename InT> struct InVec { static constexpr int VE = 16 / sizeof(InT); };
@@ -446,16 +533,6 @@ __device__ __forceinline__ void unpack(const uint4 &w, float (&f)[8], const uint
         f[2 * k] = __uint_as_float(a[k] << 16);
         f[2 * k + 1] = __uint_as_float(a[k] & 0xFFFF0000u);
     }
-}
-
-constexpr float kTinyScale = 8.673617379884035e-19f;   // 2^-60
-
-// Sum over an aligned quad with DPP adds (fused v_add_f32_dpp).
-__device__ __forceinline__ float quad_sum_dpp(float v)
-{
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-    return v;
 }
 
 // Sum over an aligned group of G lanes (G = 2, 4 or 8) with DPP adds.
@@ -496,25 +573,40 @@ template <int n> __device__ __forceinline__ void lds_load(const float *p, float 
     }
 }
 
-// Per-token operands of the token loop for one lane: its CPL columns of k^
-// and q, e at its row, and the token's scalars.
-template <int CPL> struct TokOps {
-    float k[CPL];
-    float q[CPL];
-    float e;
-    float4 s;
-};
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void st4(float *p, float a, float b, float c, float d)
+{
+    *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
 
-template <int D, int LPR, int T, bool BEFORE, typename InT>
-__global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
+// Order this wave's LDS writes before its later LDS reads by other lanes of
+// the same wave (LDS operations of one wave complete in issue order).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Value of the lane N places lower in the same 16-lane row; 1 where that
+// lane lies outside the row (DPP row_shr with the old value kept).
+template <int N> __device__ __forceinline__ float row_shr_fill1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v),
+                                                      0x110 + N, 0xF, 0xF, false));
+}
+
+template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT>
+__global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
     float eps, int chunk_row, int chunk_col, unsigned flags, int nchains)
 {
-    using Cfg = MCfg<D, LPR, T>;
-    constexpr int NT = Cfg::NT, NW = Cfg::NW, ROWS = Cfg::ROWS, LDP = Cfg::LDP,
-                  CPL = Cfg::CPL, KS = Cfg::KS, TP = Cfg::TP, NTC = Cfg::NTC;
+    using Cfg = MCfg<D, NW, T, HAS_Q>;
+    constexpr int NT = Cfg::NT, ROWS = Cfg::ROWS, LDP = Cfg::LDP, KS = Cfg::KS,
+                  NTC = Cfg::NTC, ETS = Cfg::ETS, WS = Cfg::WS, JS = Cfg::JS, NJ = Cfg::NJ,
+                  CW = Cfg::CW;
     constexpr int VE = InVec<InT>::VE;
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
     constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
@@ -522,16 +614,27 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
     static_assert(RT % NW == 0, "refresh tiles split evenly over waves");
     constexpr int RTW = RT / NW;                       // refresh tiles per wave
 
-    __shared__ __align__(16) float Bs[ROWS * LDP];     // boundary rows M_c, M_k, M_v, m_eta, m_alpha
-    __shared__ __align__(16) float Xs[T * LDP];        // x_t (MFMA operand)
-    __shared__ __align__(16) float KZ[T * LDP];        // k (generation), then z_t (readout)
-    __shared__ __align__(16) float Es[TP * LDP];       // v, then e = k^ - v
-    __shared__ __align__(16) float QVa[TP * D];        // q_t (token loop)
-    __shared__ __align__(16) float KHa[TP * D];        // k^_t (token loop)
-    __shared__ __align__(16) float4 Sx[TP];            // alpha_t, eta''_t, k^_{t-1} . k^_t, -
-    __shared__ __align__(16) float4 Sy[TP];            // c_{t-1}, eta''_t / c_t, c_t, k^_{t-1} . k^_t
-    __shared__ __align__(16) float Qt[D * LDP];        // Q_L^T at the chunk end
-    __shared__ int s_fast;
+    __shared__ __align__(16) float pool[Cfg::POOL];
+    float *const Bs = pool + Cfg::O_BS;    // boundary rows M_c, M_k, M_v, m_eta, m_alpha
+    float *const Xs = pool + Cfg::O_XS;    // x_t rows
+    float *const KZ = pool + Cfg::O_KZ;    // k rows (generation), then z_t rows (readout)
+    float *const Lc = pool + Cfg::O_KZ;    // per window L^T [s][t] (window tables)
+    float *const Es = pool + Cfg::O_ES;    // v rows (generation)
+    float *const Nn = pool + Cfg::O_ES;    // per window N [t][s] (window tables, update)
+    float *const Tp = pool + Cfg::O_ES + Cfg::SZ_NN;   // per window T', tp_index layout
+    float *const KHa = pool + Cfg::O_KH;   // k^_t rows
+    float *const Et = pool + Cfg::O_ET;    // e = k^ - v, [channel][token]
+    float *const AL = pool + Cfg::O_AL;    // alpha_t (1 on padding tokens)
+    float *const EH = pool + Cfg::O_EH;    // eta''_t (0 on padding tokens)
+    float *const GA = pool + Cfg::O_GA;    // G_{t-1}
+    float *const GZ = pool + Cfg::O_GZ;    // readout scale: G_t (G_{t-1} when reading before the write)
+    float *const RB = pool + Cfg::O_RB;    // R[15][t] of the token's window
+    float *const WG = pool + Cfg::O_WG;    // G_15 per window
+    float *const PI = pool + Cfg::O_PI;    // G_t (window tables)
+    float *const XB = pool + Cfg::O_XB;    // partial products exchanged between column halves
+    float *const QVa = pool + Cfg::O_QV;   // separate query rows q_t (HAS_Q)
+    float *const Qt = pool + Cfg::O_QT;    // Q_L^T at a chunk end
+    const float *const QR = HAS_Q ? QVa : Xs;   // query rows
 
     const int chain = xcd_remap(blockIdx.x, gridDim.x);
     if (chain >= nchains)
@@ -549,22 +652,10 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lm = lane & 15, lk = lane >> 4;        // MFMA operand row / k block
-    const int row = tid / LPR, part = tid % LPR;      // token-loop row of Q and column part
 
     const float *st = states + (static_cast<size_t>(r) * heads + h) * (ROWS * D);
     for (int idx = tid; idx < ROWS * D; idx += NT)
         Bs[(idx / D) * LDP + idx % D] = st[idx];
-    // the two pad rows are read (never used) by the prefetch of the last tokens
-    for (int idx = tid; idx < 2 * LDP; idx += NT)
-        Es[T * LDP + idx] = 0.f;
-    for (int idx = tid; idx < 2 * D; idx += NT) {
-        QVa[T * D + idx] = 0.f;
-        KHa[T * D + idx] = 0.f;
-    }
-    if (tid < 2) {
-        Sx[T + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-        Sy[T + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
 
     const size_t xbase = static_cast<size_t>(b) * N * C + static_cast<size_t>(h) * D;
     uint4 pre[NPF], preq[NPF];
@@ -578,17 +669,25 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                 route_cell32(r, H, W, N, s + u, i, j);
                 const size_t off = xbase + static_cast<size_t>(i * W + j) * C + sg * VE;
                 pre[k] = *reinterpret_cast<const uint4 *>(x + off);
-                if (q)
+                if (HAS_Q)
                     preq[k] = *reinterpret_cast<const uint4 *>(q + off);
             }
         }
     };
 
-    float P[CPL];
+    // Q^T of this wave's block of Q (wave < CW, it = wave % NTC, jg = wave / NTC):
+    // tile jl holds Q^T[16 jt + 4 lk + i][16 it + lm] in register i, with
+    // jt = jg NJ + jl. Q = I at a boundary.
+    v4f qacc[NJ];
+    auto reset_q = [&]() {
+        const int it = wave % NTC, jg = wave / NTC;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-        P[c] = (part * CPL + c == row) ? 1.0f : 0.0f;
-    float cq = 1.0f;
+        for (int jl = 0; jl < NJ; ++jl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qacc[jl][i] = (16 * (jg * NJ + jl) + 4 * lk + i == 16 * it + lm) ? 1.0f : 0.0f;
+    };
+    reset_q();
 
     const size_t out_row0 = (static_cast<size_t>(slot) * B + b) * N;
 
@@ -599,7 +698,7 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
     issue_loads(s0, nt);
 
     while (true) {
-        __syncthreads();   // previous sub-block is done with Xs, QVa, KZ; Bs is current
+        __syncthreads();   // previous sub-block is done with every token array; Bs is current
 
         // (1) store the prefetched tokens (zero rows past nt)
 #pragma unroll
@@ -610,20 +709,19 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                 float f[VE], fq[VE];
                 if (seg < nt * SEGS) {
                     unpack(pre[k], f, static_cast<const InT *>(nullptr));
-                    if (q)
+                    if (HAS_Q)
                         unpack(preq[k], fq, static_cast<const InT *>(nullptr));
                 } else {
 #pragma unroll
                     for (int e = 0; e < VE; ++e)
                         f[e] = fq[e] = 0.0f;
                 }
-                float4 *xd = reinterpret_cast<float4 *>(Xs + u * LDP + sg * VE);
-                float4 *qd = reinterpret_cast<float4 *>(QVa + u * D + sg * VE);
 #pragma unroll
                 for (int e = 0; e < VE / 4; ++e) {
-                    xd[e] = make_float4(f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
-                    qd[e] = q ? make_float4(fq[4 * e], fq[4 * e + 1], fq[4 * e + 2], fq[4 * e + 3])
-                              : make_float4(f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
+                    st4(Xs + u * LDP + sg * VE + 4 * e, f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
+                    if (HAS_Q)
+                        st4(QVa + u * LDP + sg * VE + 4 * e, fq[4 * e], fq[4 * e + 1], fq[4 * e + 2],
+                            fq[4 * e + 3]);
                 }
             }
         }
@@ -640,63 +738,56 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
             issue_loads(s1, nt1);
         __syncthreads();
 
-        const int ntm = (nt + 15) >> 4;   // token tiles
+        const int nwin = (nt + 15) >> 4;   // 16-token windows (= token tiles)
 
         // (2) boundary generation on MFMA: [k | v] = X [B_k; B_v]^T; wave w
         //     produces the 16-wide output tiles tn = w, w + NW, ...
-        {
-            for (int tn = wave; tn < 2 * NTC; tn += NW) {
-                float bg[KS];
-                lds_load(Bs + (D + tn * 16 + lm) * LDP + lk * KS, bg);
-                float *dst = (tn < NTC) ? KZ : Es;
-                const int oc = (tn % NTC) * 16 + lm;
-                for (int tm = 0; tm < ntm; ++tm) {
-                    float a[KS];
-                    lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tn = wave; tn < 2 * NTC; tn += NW) {
+            float bg[KS];
+            lds_load(Bs + (D + tn * 16 + lm) * LDP + lk * KS, bg);
+            float *dst = (tn < NTC) ? KZ : Es;
+            const int oc = (tn % NTC) * 16 + lm;
+            for (int tm = 0; tm < nwin; ++tm) {
+                float a[KS];
+                lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bg[s], acc, 0, 0, 0);
+                for (int s = 0; s < KS; ++s)
+                    acc = mfma4(a[s], bg[s], acc);
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
-                }
+                for (int rr = 0; rr < 4; ++rr)
+                    dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
             }
         }
         __syncthreads();
 
-        // (3) transition scalars, EPL lanes per token [SUMMARY stabilisation];
-        //     also the key Gram scalar k^_{t-1} . k^_t used by the token loop
+        // (3) transition scalars, EPL lanes per token [SUMMARY stabilisation]:
+        //     k^ = k / sqrt(|k|^2 + eps), e = k^ - v, eta = sigmoid(b_eta . x),
+        //     alpha = alpha_max sigmoid(b_alpha . x), soft cap, spectral clamp.
         {
             constexpr int EPL = NT / T;
             constexpr int ECPL = D / EPL;
             static_assert(EPL * T == NT && (EPL == 2 || EPL == 4 || EPL == 8), "epilogue lanes");
             const int u = tid / EPL, ep = tid % EPL;
+            const int c0e = ep * ECPL;
             if (u < nt) {
-                const int up = (u > 0) ? u - 1 : 0;
-                float kk[ECPL], vv[ECPL], xv[ECPL], kp[ECPL], be[ECPL], ba[ECPL];
-                lds_load(KZ + u * LDP + ep * ECPL, kk);
-                lds_load(Es + u * LDP + ep * ECPL, vv);
-                lds_load(Xs + u * LDP + ep * ECPL, xv);
-                lds_load(KZ + up * LDP + ep * ECPL, kp);
-                lds_load(Bs + 3 * D * LDP + ep * ECPL, be);
-                lds_load(Bs + (3 * D + 1) * LDP + ep * ECPL, ba);
-                float nk2 = 0.f, er = 0.f, ar = 0.f, np2 = 0.f, kdot = 0.f;
+                float kk[ECPL], vv[ECPL], xv[ECPL], be[ECPL], ba[ECPL];
+                lds_load(KZ + u * LDP + c0e, kk);
+                lds_load(Es + u * LDP + c0e, vv);
+                lds_load(Xs + u * LDP + c0e, xv);
+                lds_load(Bs + 3 * D * LDP + c0e, be);
+                lds_load(Bs + (3 * D + 1) * LDP + c0e, ba);
+                float nk2 = 0.f, er = 0.f, ar = 0.f;
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c) {
                     nk2 = fmaf(kk[c], kk[c], nk2);
-                    np2 = fmaf(kp[c], kp[c], np2);
-                    kdot = fmaf(kp[c], kk[c], kdot);
                     er = fmaf(be[c], xv[c], er);
                     ar = fmaf(ba[c], xv[c], ar);
                 }
                 nk2 = group_sum<EPL>(nk2);
-                np2 = group_sum<EPL>(np2);
-                kdot = group_sum<EPL>(kdot);
                 er = group_sum<EPL>(er);
                 ar = group_sum<EPL>(ar);
                 const float inv = __builtin_amdgcn_rsqf(nk2 + eps);
-                const float gram = kdot * inv * __builtin_amdgcn_rsqf(np2 + eps);
                 float nkh2 = 0.f, ne2 = 0.f;
                 float khv[ECPL], evv[ECPL];
 #pragma unroll
@@ -706,13 +797,13 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                     nkh2 = fmaf(khv[c], khv[c], nkh2);
                     ne2 = fmaf(evv[c], evv[c], ne2);
                 }
-                float4 *kd = reinterpret_cast<float4 *>(KHa + u * D + ep * ECPL);
-                float4 *ed = reinterpret_cast<float4 *>(Es + u * LDP + ep * ECPL);
 #pragma unroll
-                for (int c4 = 0; c4 < ECPL / 4; ++c4) {
-                    kd[c4] = make_float4(khv[4 * c4], khv[4 * c4 + 1], khv[4 * c4 + 2], khv[4 * c4 + 3]);
-                    ed[c4] = make_float4(evv[4 * c4], evv[4 * c4 + 1], evv[4 * c4 + 2], evv[4 * c4 + 3]);
-                }
+                for (int c4 = 0; c4 < ECPL / 4; ++c4)
+                    st4(KHa + u * LDP + c0e + 4 * c4, khv[4 * c4], khv[4 * c4 + 1], khv[4 * c4 + 2],
+                        khv[4 * c4 + 3]);
+#pragma unroll
+                for (int c = 0; c < ECPL; ++c)
+                    Et[(c0e + c) * ETS + u] = evv[c];
                 nkh2 = group_sum<EPL>(nkh2);
                 ne2 = group_sum<EPL>(ne2);
                 const float eta = sigmoidf(er);
@@ -737,138 +828,230 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                     if (cap < eta2)
                         eta2 = cap;
                 }
-                if (ep == 0)
-                    Sx[u] = make_float4(alpha, eta2, gram, 0.f);
+                if (ep == 0) {
+                    AL[u] = alpha;
+                    EH[u] = eta2;
+                }
+            } else {
+                // padding token: leaves Q unchanged
+#pragma unroll
+                for (int c4 = 0; c4 < ECPL / 4; ++c4)
+                    st4(KHa + u * LDP + c0e + 4 * c4, 0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int c = 0; c < ECPL; ++c)
+                    Et[(c0e + c) * ETS + u] = 0.f;
+                if (ep == 0) {
+                    AL[u] = 1.0f;
+                    EH[u] = 0.0f;
+                }
             }
         }
         __syncthreads();
 
-        // (3b) running retention products of the sub-block (wave 0, lane = token):
-        //      c_t = alpha_0 ... alpha_t, with the sub-block starting at scale 1.
-        //      If c stays above 2^-60 the token loop takes the fast form.
-        if (wave == 0) {
-            const float4 sx = Sx[(lane < nt) ? lane : 0];
-            float cprod = (lane < nt) ? sx.x : 1.0f;
+        // (4) window tables, wave w for windows w, w + NW, ... (window-local
+        //     token indices t, s in 0..15; lane holds s = 4 lk + i, t = lm)
+        for (int win = wave; win < nwin; win += NW) {
+            const int tb = 16 * win;
+            // Gram matrices on MFMA: gkk[i] = k^_s . k^_t, gqk[i] = k^_s . q_t
+            v4f gkk = {0.f, 0.f, 0.f, 0.f}, gqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(cprod, off);
-                if (lane >= off)
-                    cprod *= o;
+            for (int jt = 0; jt < NTC; ++jt) {
+                const float4 kv = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                const float4 qv = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                gkk = mfma16(kv, kv, gkk);
+                gqk = mfma16(kv, qv, gqk);
             }
-            float cprev = __shfl_up(cprod, 1);
-            if (lane == 0)
-                cprev = 1.0f;
-            const float clast = __shfl(cprod, nt - 1);
-            if (lane < nt)
-                Sy[lane] = make_float4(cprev, sx.y * __builtin_amdgcn_rcpf(cprod), cprod, sx.z);
-            if (lane == 0)
-                s_fast = clast >= kTinyScale;
-        }
-        __syncthreads();
+            const int t = lm;
+            const float at = AL[tb + t], et = EH[tb + t];
+            // prefix products pi = G_t over the window (each 16-lane row holds
+            // the whole window; DPP row shifts with 1 shifted in)
+            float pi = at;
+            pi *= row_shr_fill1<1>(pi);
+            pi *= row_shr_fill1<2>(pi);
+            pi *= row_shr_fill1<4>(pi);
+            pi *= row_shr_fill1<8>(pi);
+            const float gprev = row_shr_fill1<1>(pi);   // G_{t-1}
+            const float gtot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pi), 15));
+            // P[i] = R[t-1][s], Rr[i] = R[t][s] for s = 4 lk + i < t
+            float P[4], Rr[4];
+            if (gtot >= 0x1p-100f) {
+                // every prefix product is >= 2^-100: ratios are safe
+                if (lk == 0)
+                    PI[tb + t] = pi;
+                wave_lds_sync();
+                const float4 ps = ld4(PI + tb + 4 * lk);
+                const float q4[4] = {__builtin_amdgcn_rcpf(ps.x), __builtin_amdgcn_rcpf(ps.y),
+                                     __builtin_amdgcn_rcpf(ps.z), __builtin_amdgcn_rcpf(ps.w)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    P[i] = gprev * q4[i];
+                    Rr[i] = pi * q4[i];
+                }
+            } else {
+                // direct products (a prefix product underflows): p3 = product of
+                // alpha_j over 4 lk + 4 <= j < t
+                float av[16];
+                lds_load(AL + tb, av);
+                float p3 = 1.0f;
+                const int sb = 4 * lk + 4;
+#pragma unroll
+                for (int j = 4; j < 15; ++j)
+                    p3 *= (j >= sb && j < t) ? av[j] : 1.0f;
+                const float4 as4 = ld4(AL + tb + 4 * lk);
+                P[3] = p3;
+                P[2] = P[3] * ((4 * lk + 3 < t) ? as4.w : 1.0f);
+                P[1] = P[2] * ((4 * lk + 2 < t) ? as4.z : 1.0f);
+                P[0] = P[1] * ((4 * lk + 1 < t) ? as4.y : 1.0f);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Rr[i] = P[i] * at;
+            }
+            float Nr[4];
+            float *lc = Lc + win * 256;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * lk + i;
+                const bool lt = s < t;
+                Rr[i] = lt ? Rr[i] : (s == t ? 1.0f : 0.0f);
+                lc[s * 16 + t] = lt ? et * P[i] * gkk[i] : 0.0f;
+                Nr[i] = BEFORE ? (lt ? P[i] * gqk[i] : 0.0f) : Rr[i] * gqk[i];
+            }
+            st4(Nn + win * 16 * WS + t * WS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
+            if (t == 15)
+                st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
+            if (lk == 0) {
+                GA[tb + t] = gprev;
+                GZ[tb + t] = BEFORE ? gprev : pi;
+                if (t == 15)
+                    WG[win] = pi;
+            }
+            wave_lds_sync();
 
-        // (4) token-order update, LPR lanes per row of Q = cq P, CPL columns per
-        //     lane. Per token t, for this lane's row:
-        //       sc = (Q_{t-1} k^_t + e_t)_row,   w = (eta''_t / c_t) sc,
-        //       P_t = P_{t-1} - w k^_t^T         (Q_t = alpha_t Q_{t-1} - eta''_t sc k^_t^T)
-        //     The next token's dot needs no fresh reduction on the critical
-        //     path: P_t . k^_{t+1} = pre - w G_{t,t+1}, with pre = P_{t-1} . k^_{t+1}
-        //     reduced one token earlier and G from the epilogue. Operands are
-        //     prefetched two tokens ahead (three rotating register buffers).
-        //     Fast form: the sub-block starts at scale 1 and uses the
-        //     precomputed c_t. General form (a running product would fall
-        //     below 2^-60): the scale is tracked token by token and folded
-        //     into P before it underflows.
-        {
-            auto run = [&](auto fast_tag) {
-                constexpr bool FAST = decltype(fast_tag)::value;
-                if (FAST) {
+            // T = (I + L)^-1 by forward substitution, lane lm holding column
+            // c = lm; accumulated column-wise so that each step's updates are
+            // independent. Columns of L are read four steps ahead.
+            // Then T'[s][c] = -eta''_c T[s][c].
+            constexpr int LA = 4;
+            float lv[15][16];
+            auto load_col = [&](int mm) {
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        P[c] *= cq;
-                    cq = 1.0f;
+                for (int g = (mm + 1) >> 2; g < 4; ++g) {
+                    const float4 v = ld4(lc + mm * 16 + 4 * g);
+                    lv[mm][4 * g] = v.x;
+                    lv[mm][4 * g + 1] = v.y;
+                    lv[mm][4 * g + 2] = v.z;
+                    lv[mm][4 * g + 3] = v.w;
                 }
-                auto load_tok = [&](int u, TokOps<CPL> &o) {
-                    lds_load(KHa + u * D + part * CPL, o.k);
-                    lds_load(QVa + u * D + part * CPL, o.q);
-                    o.e = Es[u * LDP + row];
-                    o.s = FAST ? Sy[u] : Sx[u];
-                };
-                TokOps<CPL> t0, t1, t2;
-                load_tok(0, t0);
-                load_tok(1, t1);
-                float dk = 0.f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    dk = fmaf(P[c], t0.k[c], dk);
-                dk = group_sum<LPR>(dk);
-                auto step = [&](int u, TokOps<CPL> &cur, TokOps<CPL> &nxt, TokOps<CPL> &nn) {
-                    load_tok(u + 2, nn);
-                    float p = 0.f, zb = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        p = fmaf(P[c], nxt.k[c], p);
-                        if (BEFORE)
-                            zb = fmaf(P[c], cur.q[c], zb);
-                    }
-                    const float pre = group_sum<LPR>(p);
-                    float z = 0.f, w, fold = 1.0f, gnext;
-                    if (FAST) {
-                        const float sc = fmaf(cur.s.x, dk, cur.e);
-                        w = cur.s.y * sc;
-                        if (BEFORE)
-                            z = cur.s.x * group_sum<LPR>(zb);
-                        gnext = nxt.s.w;
-                    } else {
-                        const float sc = fmaf(cq, dk, cur.e);
-                        const float cn = cq * cur.s.x;
-                        const bool small = cn < kTinyScale;
-                        const float cqn = small ? 1.0f : cn;
-                        fold = small ? cn : 1.0f;
-                        w = cur.s.y * __builtin_amdgcn_rcpf(cqn) * sc;
-                        if (BEFORE)
-                            z = cq * group_sum<LPR>(zb);
-                        if (small) {
-#pragma unroll
-                            for (int c = 0; c < CPL; ++c)
-                                P[c] *= cn;
-                        }
-                        cq = cqn;
-                        gnext = nxt.s.z;
-                    }
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        P[c] = fmaf(-w, cur.k[c], P[c]);
-                    if (!BEFORE) {
-                        float zz = 0.f;
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c)
-                            zz = fmaf(P[c], cur.q[c], zz);
-                        z = (FAST ? cur.s.z : cq) * group_sum<LPR>(zz);
-                    }
-                    KZ[u * LDP + row] = z;   // the LPR lanes of the row store the same value
-                    dk = fmaf(-w, gnext, fold * pre);
-                };
-                int u = 0;
-                for (; u + 2 < nt; u += 3) {
-                    step(u, t0, t1, t2);
-                    step(u + 1, t1, t2, t0);
-                    step(u + 2, t2, t0, t1);
-                }
-                if (u < nt)
-                    step(u, t0, t1, t2);
-                if (u + 1 < nt)
-                    step(u + 1, t1, t2, t0);
-                if (FAST)
-                    cq = Sy[nt - 1].z;
             };
-            if (s_fast)
-                run(std::true_type{});
-            else
-                run(std::false_type{});
+#pragma unroll
+            for (int mm = 0; mm < LA; ++mm)
+                load_col(mm);
+            float xv[16];
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt)
+                xv[tt] = (tt == lm) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int mm = 0; mm < 15; ++mm) {
+                if (mm + LA < 15)
+                    load_col(mm + LA);
+#pragma unroll
+                for (int tt = mm + 1; tt < 16; ++tt)
+                    xv[tt] = fmaf(-lv[mm][tt], xv[mm], xv[tt]);
+            }
+            const float ec = -EH[tb + lm];
+            float *tp = Tp + win * 256;
+            if (lk == 0) {
+#pragma unroll
+                for (int ss = 0; ss < 16; ++ss)
+                    tp[tp_index(ss, lm)] = ec * xv[ss];
+            }
         }
         __syncthreads();
 
-        // (5) readout on MFMA: y_t = B_c z_t. With more waves than 16-wide
+        // (5) token-order update, window by window, on MFMA. Wave w owns rows
+        //     16 it .. 16 it + 15 of Q (it = w % NTC) and, when two waves share
+        //     those rows (JS = 2), the columns of its half jg = w / NTC of Q.
+        //     Per window:
+        //       A   = diag(G_{t-1}) K^ Q_0^T + E           [t][i]
+        //       U   = T' A                                 [s][i]
+        //       Z   = diag(G_t) Qrows Q_0^T + N U          [t][i]  -> z_t rows
+        //       Q^T = G_15 Q_0^T + K^^T diag(R[15]) U      [j][i]
+        //     The two halves of the contractions over j are exchanged through
+        //     LDS (double-buffered by window parity: one barrier per window).
+        if (wave < CW) {
+            const int it = wave % NTC, jg = wave / NTC;
+            for (int win = 0; win < nwin; ++win) {
+                const int tb = 16 * win;
+                v4f A = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jl = 0; jl < NJ; ++jl) {
+                    const int jt = jg * NJ + jl;
+                    const float4 kv = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                    const float4 qv = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                    A = mfma16(kv, qacc[jl], A);
+                    Z = mfma16(qv, qacc[jl], Z);
+                }
+                if (JS == 2) {
+                    float *xb = XB + ((win & 1) * NTC + it) * 768 + 4 * lane;
+                    st4(xb + 256 * jg, A[0], A[1], A[2], A[3]);
+                    if (jg == 1)
+                        st4(xb + 512, Z[0], Z[1], Z[2], Z[3]);
+                    __syncthreads();
+                    const float4 pa = ld4(xb + 256 * (1 - jg));
+                    A[0] += pa.x;
+                    A[1] += pa.y;
+                    A[2] += pa.z;
+                    A[3] += pa.w;
+                    if (jg == 0) {
+                        const float4 pz = ld4(xb + 512);
+                        Z[0] += pz.x;
+                        Z[1] += pz.y;
+                        Z[2] += pz.z;
+                        Z[3] += pz.w;
+                    }
+                }
+                const float4 ga = ld4(GA + tb + 4 * lk);
+                const float4 ee = ld4(Et + (16 * it + lm) * ETS + tb + 4 * lk);
+                A[0] = fmaf(ga.x, A[0], ee.x);
+                A[1] = fmaf(ga.y, A[1], ee.y);
+                A[2] = fmaf(ga.z, A[2], ee.z);
+                A[3] = fmaf(ga.w, A[3], ee.w);
+                const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
+                v4f U = {0.f, 0.f, 0.f, 0.f};
+                U = mfma16(tpv, A, U);
+                if (jg == 0) {
+                    const float4 gz = ld4(GZ + tb + 4 * lk);
+                    Z[0] *= gz.x;
+                    Z[1] *= gz.y;
+                    Z[2] *= gz.z;
+                    Z[3] *= gz.w;
+                    const float4 nnv = ld4(Nn + win * 16 * WS + lm * WS + 4 * lk);
+                    Z = mfma16(nnv, U, Z);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        KZ[(tb + 4 * lk + i) * LDP + 16 * it + lm] = Z[i];
+                }
+                const float4 rb = ld4(RB + tb + 4 * lk);
+                U[0] *= rb.x;
+                U[1] *= rb.y;
+                U[2] *= rb.z;
+                U[3] *= rb.w;
+                const float wg = WG[win];
+#pragma unroll
+                for (int jl = 0; jl < NJ; ++jl) {
+                    const int jt = jg * NJ + jl;
+                    const float4 kt = make_float4(KHa[(tb + 4 * lk) * LDP + 16 * jt + lm],
+                                                  KHa[(tb + 4 * lk + 1) * LDP + 16 * jt + lm],
+                                                  KHa[(tb + 4 * lk + 2) * LDP + 16 * jt + lm],
+                                                  KHa[(tb + 4 * lk + 3) * LDP + 16 * jt + lm]);
+                    qacc[jl] *= wg;
+                    qacc[jl] = mfma16(kt, U, qacc[jl]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // (6) readout on MFMA: y_t = B_c z_t. With more waves than 16-wide
         //     channel tiles, wave w takes the token tiles tm = w, w + NW, ... and
         //     writes whole output rows of its head; otherwise wave w takes the
         //     channel tiles tn = w, w + NW, ... for every token tile.
@@ -876,7 +1059,7 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
             constexpr bool BY_TOKENS = NW > NTC;
             const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
             const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
-            for (int tm = tm0; tm < ntm; tm += tms) {
+            for (int tm = tm0; tm < nwin; tm += tms) {
                 float a[KS];
                 lds_load(KZ + (tm * 16 + lm) * LDP + lk * KS, a);
                 for (int tn = tn0; tn < NTC; tn += tns) {
@@ -885,7 +1068,7 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], br[s], acc, 0, 0, 0);
+                        acc = mfma4(a[s], br[s], acc);
                     float *orow = out + (out_row0 + s0) * C + static_cast<size_t>(h) * D + tn * 16 + lm;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
@@ -899,10 +1082,15 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
 
         if (chunk_end) {
             if (cend < N) {
-                // (6) refresh the boundary: B <- B Q_L (tiles split over the waves)
+                // (7) refresh the boundary: B <- B Q_L (tiles split over the waves)
+                if (wave < CW) {
+                    const int it = wave % NTC, jg = wave / NTC;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    Qt[(part * CPL + c) * LDP + row] = cq * P[c];
+                    for (int jl = 0; jl < NJ; ++jl)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            Qt[(16 * (jg * NJ + jl) + 4 * lk + i) * LDP + 16 * it + lm] = qacc[jl][i];
+                }
                 __syncthreads();
                 v4f racc[RTW];
 #pragma unroll
@@ -915,7 +1103,7 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bq[s], acc, 0, 0, 0);
+                        acc = mfma4(a[s], bq[s], acc);
                     racc[w] = acc;
                 }
                 float vacc = 0.f;
@@ -944,10 +1132,7 @@ __global__ __launch_bounds__(LPR * D) void scan_mfma_kernel(
                 if (tid < 2 * D)
                     Bs[(3 * D + vv) * LDP + vj] = vacc;
             }
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                P[c] = (part * CPL + c == row) ? 1.0f : 0.0f;
-            cq = 1.0f;
+            reset_q();
         }
         if (s1 >= N)
             break;
@@ -1140,9 +1325,9 @@ int grid_for(long long work, int block)
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
-// tokens per sub-block and lanes per row of Q of the MFMA scan kernel
+// waves per chain and tokens per sub-block of the MFMA scan kernel
+template <int D> struct MfmaNW { static constexpr int value = 4; };
 template <int D> struct MfmaT { static constexpr int value = (D == 32) ? 64 : 32; };
-template <int D> struct MfmaLPR { static constexpr int value = (D == 32) ? 8 : 4; };
 
 template <int D, typename InT>
 srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W, int C,
@@ -1156,17 +1341,20 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
     hipStream_t st = static_cast<hipStream_t>(p->stream);
     if constexpr (D >= 32) {
         constexpr int T = MfmaT<D>::value;
-        constexpr int LPR = MfmaLPR<D>::value;
-        if (p->flags & F_READ_BEFORE)
-            hipLaunchKernelGGL((scan_mfma_kernel<D, LPR, T, true, InT>), dim3(nblocks), dim3(LPR * D), 0,
-                               st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+        constexpr int NW = MfmaNW<D>::value;
+        const bool before = (p->flags & F_READ_BEFORE) != 0, has_q = p->q != nullptr;
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(nblocks), dim3(NW * 64), 0, st,
+                               static_cast<const InT *>(x), static_cast<const InT *>(p->q),
                                p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
                                p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+        };
+        if (before)
+            has_q ? go(scan_mfma_kernel<D, NW, T, true, true, InT>)
+                  : go(scan_mfma_kernel<D, NW, T, true, false, InT>);
         else
-            hipLaunchKernelGGL((scan_mfma_kernel<D, LPR, T, false, InT>), dim3(nblocks), dim3(LPR * D), 0,
-                               st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
-                               p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
-                               p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+            has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT>)
+                  : go(scan_mfma_kernel<D, NW, T, false, false, InT>);
         return launch_check("scan_mfma_kernel");
     } else {
         hipLaunchKernelGGL((scan_simple_kernel<D, InT>), dim3(nblocks), dim3(ScanCfg<D>::NT), 0,
