@@ -440,6 +440,48 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// bf16 operands of v_mfma_f32_16x16x32_bf16: 8 per lane. Lane l supplies
+// reduction indices k = 8 (l / 16) + e, e = 0..7, for both operands.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Eight floats that are exactly representable in bf16, packed as bf16.
+__device__ __forceinline__ bf16x8 pack_bf16_exact(const float (&v)[8])
+{
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (__float_as_uint(v[2 * k]) >> 16) | (__float_as_uint(v[2 * k + 1]) & 0xFFFF0000u);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Exact split of eight floats into three bf16 parts, v = hi + mid + lo:
+// truncation to bf16 keeps the leading 8 significant bits, so three parts
+// hold all 24 bits of an fp32 significand (each residual is exact in fp32).
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], bf16x8 &hi, bf16x8 &mid, bf16x8 &lo)
+{
+    u32x4 wh, wm, wl;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t h[2], m[2], l[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float x = v[2 * k + e];
+            h[e] = __float_as_uint(x) & 0xFFFF0000u;
+            const float r = x - __uint_as_float(h[e]);
+            m[e] = __float_as_uint(r) & 0xFFFF0000u;
+            const float r2 = r - __uint_as_float(m[e]);
+            l[e] = __float_as_uint(r2) & 0xFFFF0000u;
+        }
+        wh[k] = (h[0] >> 16) | h[1];
+        wm[k] = (m[0] >> 16) | m[1];
+        wl[k] = (l[0] >> 16) | l[1];
+    }
+    hi = __builtin_bit_cast(bf16x8, wh);
+    mid = __builtin_bit_cast(bf16x8, wm);
+    lo = __builtin_bit_cast(bf16x8, wl);
+}
+
 // c += A B over one 16-wide block of the reduction index (4 instructions)
 __device__ __forceinline__ v4f mfma16(const float4 &a, const float4 &b, v4f c)
 {
@@ -478,7 +520,7 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
 
     // LDS pool (floats). Arrays that are dead in a phase lend their space:
     // the k rows (dead after the epilogue, until the update writes z) hold
-    // the windows' L^T tables; the v rows (dead after the epilogue) hold the
+    // the windows' L tables; the v rows (dead after the epilogue) hold the
     // N and T' tables, and at a chunk end Q_L^T when it fits.
     static constexpr int SZ_TOK = T * LDP;
     static constexpr int SZ_LC = NWIN * 256;
@@ -501,8 +543,9 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int O_WG = O_RB + T;
     static constexpr int O_PI = O_WG + 4;
     static constexpr int O_XB = O_PI + T;
-    static constexpr int SZ_XB = (JS == 2) ? 2 * NTC * 768 : 0;
-    static constexpr int O_QV = O_XB + SZ_XB;
+    static constexpr int SZ_XB = (JS == 2) ? 2 * NTC * 512 : 0;
+    static constexpr int O_KZ2 = O_XB + SZ_XB;
+    static constexpr int O_QV = O_KZ2 + ((JS == 2) ? SZ_TOK : 0);
     static constexpr int O_QT = QT_IN_ES ? O_ES : O_QV + (HAS_Q ? SZ_TOK : 0);
     static constexpr int POOL = (QT_IN_ES ? O_QV : O_QT + SZ_QT) + (HAS_Q ? SZ_TOK : 0);
 };
@@ -596,6 +639,18 @@ template <int N> __device__ __forceinline__ float row_shr_fill1(float v)
                                                       0x110 + N, 0xF, 0xF, false));
 }
 
+// Value of lane `src` (0..3) of each aligned quad, in every lane of the quad.
+__device__ __forceinline__ float quad_bcast(float v, int src)
+{
+    const int ctrl = src * 0x55;   // quad_perm [src, src, src, src]
+    switch (ctrl) {
+    case 0x00: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x00, 0xF, 0xF, false));
+    case 0x55: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55, 0xF, 0xF, false));
+    case 0xAA: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xFF, 0xF, 0xF, false));
+    }
+}
+
 template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT>
 __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
@@ -606,7 +661,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     using Cfg = MCfg<D, NW, T, HAS_Q>;
     constexpr int NT = Cfg::NT, ROWS = Cfg::ROWS, LDP = Cfg::LDP, KS = Cfg::KS,
                   NTC = Cfg::NTC, ETS = Cfg::ETS, WS = Cfg::WS, JS = Cfg::JS, NJ = Cfg::NJ,
-                  CW = Cfg::CW;
+                  CW = Cfg::CW, NWIN = Cfg::NWIN;
     constexpr int VE = InVec<InT>::VE;
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
     constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
@@ -618,7 +673,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const Bs = pool + Cfg::O_BS;    // boundary rows M_c, M_k, M_v, m_eta, m_alpha
     float *const Xs = pool + Cfg::O_XS;    // x_t rows
     float *const KZ = pool + Cfg::O_KZ;    // k rows (generation), then z_t rows (readout)
-    float *const Lc = pool + Cfg::O_KZ;    // per window L^T [s][t] (window tables)
+    float *const Lc = pool + Cfg::O_KZ;    // per window L [t][s] (window tables)
     float *const Es = pool + Cfg::O_ES;    // v rows (generation)
     float *const Nn = pool + Cfg::O_ES;    // per window N [t][s] (window tables, update)
     float *const Tp = pool + Cfg::O_ES + Cfg::SZ_NN;   // per window T', tp_index layout
@@ -632,6 +687,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const WG = pool + Cfg::O_WG;    // G_15 per window
     float *const PI = pool + Cfg::O_PI;    // G_t (window tables)
     float *const XB = pool + Cfg::O_XB;    // partial products exchanged between column halves
+    float *const KZ2 = pool + Cfg::O_KZ2;  // second partial sum of the z_t rows (JS = 2)
     float *const QVa = pool + Cfg::O_QV;   // separate query rows q_t (HAS_Q)
     float *const Qt = pool + Cfg::O_QT;    // Q_L^T at a chunk end
     const float *const QR = HAS_Q ? QVa : Xs;   // query rows
@@ -741,22 +797,62 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         const int nwin = (nt + 15) >> 4;   // 16-token windows (= token tiles)
 
         // (2) boundary generation on MFMA: [k | v] = X [B_k; B_v]^T; wave w
-        //     produces the 16-wide output tiles tn = w, w + NW, ...
+        //     produces the 16-wide output tiles tn = w, w + NW, ... With bf16
+        //     input, x is exact in bf16 and each boundary row is split exactly
+        //     into three bf16 parts, so three bf16 products (16x16x32) per
+        //     32-wide block give the fp32 result at a third of the cost of the
+        //     fp32 instruction.
         for (int tn = wave; tn < 2 * NTC; tn += NW) {
-            float bg[KS];
-            lds_load(Bs + (D + tn * 16 + lm) * LDP + lk * KS, bg);
             float *dst = (tn < NTC) ? KZ : Es;
             const int oc = (tn % NTC) * 16 + lm;
-            for (int tm = 0; tm < nwin; ++tm) {
-                float a[KS];
-                lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
+            const float *brow = Bs + (D + tn * 16 + lm) * LDP;
+            if constexpr (std::is_same<InT, uint16_t>::value) {
+                constexpr int KB = D / 32;
+                bf16x8 bh[KB], bm[KB], bl[KB];
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = mfma4(a[s], bg[s], acc);
+                for (int kb = 0; kb < KB; ++kb) {
+                    float bv[8];
+                    lds_load(brow + 32 * kb + 8 * lk, bv);
+                    split3_bf16(bv, bh[kb], bm[kb], bl[kb]);
+                }
+                // every token tile of the sub-block (rows past nt are zero)
+                bf16x8 xa[NWIN][KB];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+                for (int tm = 0; tm < NWIN; ++tm)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        float xv[8];
+                        lds_load(Xs + (tm * 16 + lm) * LDP + 32 * kb + 8 * lk, xv);
+                        xa[tm][kb] = pack_bf16_exact(xv);
+                    }
+#pragma unroll
+                for (int tm = 0; tm < NWIN; ++tm) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bl[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bm[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bh[kb], acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+                }
+            } else {
+                float bg[KS];
+                lds_load(brow + lk * KS, bg);
+#pragma unroll
+                for (int tm = 0; tm < NWIN; ++tm) {
+                    float a[KS];
+                    lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        acc = mfma4(a[s], bg[s], acc);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+                }
             }
         }
         __syncthreads();
@@ -906,16 +1002,17 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 for (int i = 0; i < 4; ++i)
                     Rr[i] = P[i] * at;
             }
-            float Nr[4];
+            float Nr[4], Lr[4];
             float *lc = Lc + win * 256;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 4 * lk + i;
                 const bool lt = s < t;
                 Rr[i] = lt ? Rr[i] : (s == t ? 1.0f : 0.0f);
-                lc[s * 16 + t] = lt ? et * P[i] * gkk[i] : 0.0f;
+                Lr[i] = lt ? et * P[i] * gkk[i] : 0.0f;
                 Nr[i] = BEFORE ? (lt ? P[i] * gqk[i] : 0.0f) : Rr[i] * gqk[i];
             }
+            st4(lc + t * 16 + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
             st4(Nn + win * 16 * WS + t * WS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
             if (t == 15)
                 st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
@@ -927,43 +1024,52 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
             wave_lds_sync();
 
-            // T = (I + L)^-1 by forward substitution, lane lm holding column
-            // c = lm; accumulated column-wise so that each step's updates are
-            // independent. Columns of L are read four steps ahead.
-            // Then T'[s][c] = -eta''_c T[s][c].
-            constexpr int LA = 4;
-            float lv[15][16];
-            auto load_col = [&](int mm) {
+            // T = (I + L)^-1 by block forward substitution over 4 x 4 blocks:
+            // lane 4 c + g holds rows 4 g .. 4 g + 3 of column c of T. For each
+            // block b in turn, the lanes of block b finish their four rows, the
+            // quad broadcasts them (DPP), and the lanes of later blocks fold
+            // them into their partial sums. Then T'[s][c] = -eta''_c T[s][c].
+            {
+                const int c = lane >> 2, g = lane & 3;
+                float lrow[4][16];   // L[4 g + i][m]
 #pragma unroll
-                for (int g = (mm + 1) >> 2; g < 4; ++g) {
-                    const float4 v = ld4(lc + mm * 16 + 4 * g);
-                    lv[mm][4 * g] = v.x;
-                    lv[mm][4 * g + 1] = v.y;
-                    lv[mm][4 * g + 2] = v.z;
-                    lv[mm][4 * g + 3] = v.w;
+                for (int i = 0; i < 4; ++i)
+                    lds_load(lc + (4 * g + i) * 16, lrow[i]);
+                float acc[4], xf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[i] = (4 * g + i == c) ? 1.0f : 0.0f;
+                    xf[i] = 0.0f;
                 }
-            };
 #pragma unroll
-            for (int mm = 0; mm < LA; ++mm)
-                load_col(mm);
-            float xv[16];
+                for (int bb = 0; bb < 4; ++bb) {
+                    // rows of block bb (final in the lanes with g == bb)
+                    float xs[4];
+                    xs[0] = acc[0];
+                    xs[1] = fmaf(-lrow[1][4 * bb], xs[0], acc[1]);
+                    xs[2] = fmaf(-lrow[2][4 * bb + 1], xs[1], fmaf(-lrow[2][4 * bb], xs[0], acc[2]));
+                    xs[3] = fmaf(-lrow[3][4 * bb + 2], xs[2],
+                                 fmaf(-lrow[3][4 * bb + 1], xs[1], fmaf(-lrow[3][4 * bb], xs[0], acc[3])));
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt)
-                xv[tt] = (tt == lm) ? 1.0f : 0.0f;
+                    for (int i = 0; i < 4; ++i)
+                        xf[i] = (g == bb) ? xs[i] : xf[i];
+                    if (bb < 3) {
+                        float xb[4];
 #pragma unroll
-            for (int mm = 0; mm < 15; ++mm) {
-                if (mm + LA < 15)
-                    load_col(mm + LA);
+                        for (int i = 0; i < 4; ++i)
+                            xb[i] = quad_bcast(xs[i], bb);
 #pragma unroll
-                for (int tt = mm + 1; tt < 16; ++tt)
-                    xv[tt] = fmaf(-lv[mm][tt], xv[mm], xv[tt]);
-            }
-            const float ec = -EH[tb + lm];
-            float *tp = Tp + win * 256;
-            if (lk == 0) {
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int ss = 0; ss < 16; ++ss)
-                    tp[tp_index(ss, lm)] = ec * xv[ss];
+                            for (int j = 0; j < 4; ++j)
+                                acc[i] = fmaf(-lrow[i][4 * bb + j], xb[j], acc[i]);
+                    }
+                }
+                const float ec = -EH[tb + c];
+                float *tp = Tp + win * 256;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tp[tp_index(4 * g + i, c)] = ec * xf[i];
             }
         }
         __syncthreads();
@@ -976,85 +1082,101 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //       U   = T' A                                 [s][i]
         //       Z   = diag(G_t) Qrows Q_0^T + N U          [t][i]  -> z_t rows
         //       Q^T = G_15 Q_0^T + K^^T diag(R[15]) U      [j][i]
-        //     The two halves of the contractions over j are exchanged through
-        //     LDS (double-buffered by window parity: one barrier per window).
+        //     With JS = 2 the contraction over j in A is completed by
+        //     exchanging the halves through LDS (double-buffered by window
+        //     parity: one barrier per window); Z is left as two partial sums
+        //     (each wave also takes half of the N U terms) that the readout adds.
         if (wave < CW) {
             const int it = wave % NTC, jg = wave / NTC;
+            float4 kv[NJ], qv[NJ];
+            auto load_rows = [&](int tb) {
+#pragma unroll
+                for (int jl = 0; jl < NJ; ++jl) {
+                    const int jt = jg * NJ + jl;
+                    kv[jl] = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                    qv[jl] = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                }
+            };
+            if (nwin > 0)
+                load_rows(0);
             for (int win = 0; win < nwin; ++win) {
                 const int tb = 16 * win;
                 v4f A = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
+                    A = mfma16(kv[jl], qacc[jl], A);
+                    Z = mfma16(qv[jl], qacc[jl], Z);
+                }
+                const float4 ga = ld4(GA + tb + 4 * lk);
+                const float4 gz = ld4(GZ + tb + 4 * lk);
+                const float4 rb = ld4(RB + tb + 4 * lk);
+                const float4 ee = ld4(Et + (16 * it + lm) * ETS + tb + 4 * lk);
+                const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
+                const float4 nnv = ld4(Nn + win * 16 * WS + lm * WS + 4 * lk);
+                const float wg = WG[win];
+                float4 kt[NJ];
+#pragma unroll
+                for (int jl = 0; jl < NJ; ++jl) {
                     const int jt = jg * NJ + jl;
-                    const float4 kv = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
-                    const float4 qv = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
-                    A = mfma16(kv, qacc[jl], A);
-                    Z = mfma16(qv, qacc[jl], Z);
+                    kt[jl] = make_float4(KHa[(tb + 4 * lk) * LDP + 16 * jt + lm],
+                                         KHa[(tb + 4 * lk + 1) * LDP + 16 * jt + lm],
+                                         KHa[(tb + 4 * lk + 2) * LDP + 16 * jt + lm],
+                                         KHa[(tb + 4 * lk + 3) * LDP + 16 * jt + lm]);
                 }
                 if (JS == 2) {
-                    float *xb = XB + ((win & 1) * NTC + it) * 768 + 4 * lane;
+                    float *xb = XB + ((win & 1) * NTC + it) * 512 + 4 * lane;
                     st4(xb + 256 * jg, A[0], A[1], A[2], A[3]);
-                    if (jg == 1)
-                        st4(xb + 512, Z[0], Z[1], Z[2], Z[3]);
                     __syncthreads();
                     const float4 pa = ld4(xb + 256 * (1 - jg));
                     A[0] += pa.x;
                     A[1] += pa.y;
                     A[2] += pa.z;
                     A[3] += pa.w;
-                    if (jg == 0) {
-                        const float4 pz = ld4(xb + 512);
-                        Z[0] += pz.x;
-                        Z[1] += pz.y;
-                        Z[2] += pz.z;
-                        Z[3] += pz.w;
-                    }
                 }
-                const float4 ga = ld4(GA + tb + 4 * lk);
-                const float4 ee = ld4(Et + (16 * it + lm) * ETS + tb + 4 * lk);
                 A[0] = fmaf(ga.x, A[0], ee.x);
                 A[1] = fmaf(ga.y, A[1], ee.y);
                 A[2] = fmaf(ga.z, A[2], ee.z);
                 A[3] = fmaf(ga.w, A[3], ee.w);
-                const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
                 v4f U = {0.f, 0.f, 0.f, 0.f};
                 U = mfma16(tpv, A, U);
-                if (jg == 0) {
-                    const float4 gz = ld4(GZ + tb + 4 * lk);
-                    Z[0] *= gz.x;
-                    Z[1] *= gz.y;
-                    Z[2] *= gz.z;
-                    Z[3] *= gz.w;
-                    const float4 nnv = ld4(Nn + win * 16 * WS + lm * WS + 4 * lk);
+                Z[0] *= gz.x;
+                Z[1] *= gz.y;
+                Z[2] *= gz.z;
+                Z[3] *= gz.w;
+                if (JS == 1) {
                     Z = mfma16(nnv, U, Z);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        KZ[(tb + 4 * lk + i) * LDP + 16 * it + lm] = Z[i];
+                } else if (jg == 0) {
+                    Z = mfma4(nnv.x, U[0], Z);
+                    Z = mfma4(nnv.y, U[1], Z);
+                } else {
+                    Z = mfma4(nnv.z, U[2], Z);
+                    Z = mfma4(nnv.w, U[3], Z);
                 }
-                const float4 rb = ld4(RB + tb + 4 * lk);
                 U[0] *= rb.x;
                 U[1] *= rb.y;
                 U[2] *= rb.z;
                 U[3] *= rb.w;
-                const float wg = WG[win];
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
-                    const int jt = jg * NJ + jl;
-                    const float4 kt = make_float4(KHa[(tb + 4 * lk) * LDP + 16 * jt + lm],
-                                                  KHa[(tb + 4 * lk + 1) * LDP + 16 * jt + lm],
-                                                  KHa[(tb + 4 * lk + 2) * LDP + 16 * jt + lm],
-                                                  KHa[(tb + 4 * lk + 3) * LDP + 16 * jt + lm]);
                     qacc[jl] *= wg;
-                    qacc[jl] = mfma16(kt, U, qacc[jl]);
+                    qacc[jl] = mfma16(kt[jl], U, qacc[jl]);
                 }
+                if (win + 1 < nwin)
+                    load_rows(tb + 16);
+                float *zd = (JS == 2 && jg == 1) ? KZ2 : KZ;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    zd[(tb + 4 * lk + i) * LDP + 16 * it + lm] = Z[i];
             }
         }
         __syncthreads();
 
-        // (6) readout on MFMA: y_t = B_c z_t. With more waves than 16-wide
-        //     channel tiles, wave w takes the token tiles tm = w, w + NW, ... and
-        //     writes whole output rows of its head; otherwise wave w takes the
-        //     channel tiles tn = w, w + NW, ... for every token tile.
+        // (6) readout on MFMA: Y^T = B_c Z^T, so that each lane holds four
+        //     consecutive channels of one token (16-byte stores). With more
+        //     waves than 16-wide channel tiles, wave w takes the token tiles
+        //     tm = w, w + NW, ... and writes whole output rows of its head;
+        //     otherwise wave w takes the channel tiles tn = w, w + NW, ... for
+        //     every token tile.
         {
             constexpr bool BY_TOKENS = NW > NTC;
             const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
@@ -1062,20 +1184,25 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             for (int tm = tm0; tm < nwin; tm += tms) {
                 float a[KS];
                 lds_load(KZ + (tm * 16 + lm) * LDP + lk * KS, a);
+                if (JS == 2) {
+                    float a2[KS];
+                    lds_load(KZ2 + (tm * 16 + lm) * LDP + lk * KS, a2);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        a[s] += a2[s];
+                }
+                const int u0 = tm * 16 + lm;
+                float *orow = out + (out_row0 + s0 + u0) * C + static_cast<size_t>(h) * D + 4 * lk;
+#pragma unroll
                 for (int tn = tn0; tn < NTC; tn += tns) {
                     float br[KS];
                     lds_load(Bs + (tn * 16 + lm) * LDP + lk * KS, br);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        acc = mfma4(a[s], br[s], acc);
-                    float *orow = out + (out_row0 + s0) * C + static_cast<size_t>(h) * D + tn * 16 + lm;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int u0 = tm * 16 + 4 * lk + rr;
-                        if (u0 < nt)
-                            orow[static_cast<size_t>(u0) * C] = acc[rr];
-                    }
+                        acc = mfma4(br[s], a[s], acc);
+                    if (u0 < nt)
+                        *reinterpret_cast<float4 *>(orow + tn * 16) = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }
