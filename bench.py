@@ -110,6 +110,77 @@ def cpu_baseline(wl, n_items: int):
                       f"single-threaded double-precision oracle, {dt:.1f} s"}
 
 
+def seq1d_workload():
+    """Standalone 1-D SRNL workload: B=256 sequences of 3136 tokens (the
+    56x56 token count), C=64 as 2 heads x d=32, bf16 N(0,1) input, default
+    64-token chunks, states N(0, 0.02^2), seed 6: 512 independent chains, the
+    same chain count as hier56."""
+    import numpy as np
+    from self_referential_memory_amd import synth
+    B, N, C, heads, d = 256, 3136, 64, 2, 32
+    x = synth.round_bf16(synth.normals(6, 1, B * N * C).reshape(B, N, C).astype(np.float32))[0]
+    st = synth.states(6, heads, d, 0.02)[0]
+    return x, st, heads, d
+
+
+def main_seq1d(args):
+    import numpy as np
+    import torch
+    from self_referential_memory_amd import srnl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xh, sth, heads, d = seq1d_workload()
+    B, N, C = xh.shape
+    x = torch.from_numpy(xh).to(dev).to(torch.bfloat16)
+    st = torch.from_numpy(sth).to(dev)
+    y = torch.empty((B, N, C), dtype=torch.float32, device=dev)
+    p = srnl.make_params(st, x)
+    for _ in range(args.warmup):
+        srnl.scan_1d(x, st, heads, d, out=y, params=p)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        srnl.scan_1d(x, st, heads, d, out=y, params=p)
+        b.record()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms = dt * 1000.0 / args.steps
+    units = B * N * heads
+    flops = algorithmic_flops_per_unit(d) * units
+    achieved = flops / (scan_ms / 1000.0) / 1e12
+    rec = {
+        "metric": "SRNL 1-D fwd tokens·heads/s",
+        "value": units / (ms / 1000.0),
+        "unit": "tokens·heads/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "seq1d: standalone 1-D SRNL, B=256 sequences x 3136 tokens, "
+                               "C=64 = 2 heads x d=32, 64-token chunks, bf16 input, fp32 state, "
+                               "seed 6", "B": B, "N": N, "C": C, "heads": heads, "d": d,
+                   "chunk": 64, "input_dtype": "bf16", "parallelism": "single GPU"},
+        "roofline": {"kernel": "scan_kernel", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_items, B)
+        t0 = time.perf_counter()
+        oracle.scan_1d(xh[:n], sth, heads, d)
+        dtc = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": n * N * heads / dtc, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequences 0..{n - 1} of {B}, single-threaded double-precision oracle, "
+                      f"{dtc:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +194,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="digest two rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
+    ap.add_argument("--workload", choices=("hier56", "seq1d"), default="hier56",
+                    help="hier56: the 2-D four-route operator (default); seq1d: the "
+                         "standalone 1-D SRNL")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_command)
@@ -132,6 +206,9 @@ def main():
               "(the operator's chains are independent and would shard over batch, "
               "heads and routes without communication)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "seq1d":
+        main_seq1d(args)
+        return
 
     import numpy as np
     import torch

@@ -126,6 +126,26 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
                           float *out);
 
 /*
+ * srnl_scan_1d -- standalone 1-D SRNL [README SRNL and VisionHOPE operator]:
+ * a sequence of N tokens scanned once, in token order, with the same write
+ * rule, stabilisation and readout as srnl_scan_fwd. A new sequence starts at
+ * every call. The default chunk is 64 tokens; a positive
+ * params->chunk_row overrides it, and the last chunk may be short
+ * [README SRNL and VisionHOPE operator]. params->chunk_col is ignored.
+ *
+ *   x      [B][N][C], in_dtype, device. C must equal heads * d.
+ *   params->states  [heads][3d^2+2d] fp32, device (one block: the 1-D
+ *          operator has a single direction).
+ *   params->q       [B][N][C] in in_dtype, or NULL for q = x; separate
+ *          queries must have the dtype of x [README Fast inference].
+ *   out    [B][N][C] fp32, device. Fully overwritten.
+ * Equal to srnl_scan_fwd on the 1 x N grid with route_mask = 1 and
+ * chunk_row = the chunk above. Errors: as srnl_scan_fwd.
+ */
+srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
+                         const srnl_params *params, float *out);
+
+/*
  * srnl_fuse -- restore and fuse [OVERVIEW Four-Directional Scanning and
  * Spatial Chunking; SUMMARY 2-D maps]: each route's outputs go back to
  * their grid cells and are combined with learned per-channel scales,

@@ -128,6 +128,22 @@ def scan(x, states, heads: int, d: int, route_mask: int = 15, q=None, *,
     return y
 
 
+def scan_1d(x, states, heads: int, d: int, q=None, *, chunk: int = 0, **kw):
+    """Standalone 1-D SRNL [README SRNL and VisionHOPE operator]: x [B][N][C]
+    scanned once in token order, chunks of ``chunk`` tokens (0 selects the
+    1-D default of 64; the last chunk may be short). The sequence is the
+    row-major route of a 1 x N grid, so this is ``scan`` on that grid with
+    route 0. ``states`` is [heads][3d^2+2d]. Returns y [B][N][C] in float64."""
+    x = np.asarray(x)
+    B, N, C = x.shape
+    st = np.zeros((4,) + tuple(np.shape(states)), dtype=np.float64)
+    st[0] = states
+    qq = None if q is None else np.asarray(q).reshape(B, 1, N, C)
+    y = scan(x.reshape(B, 1, N, C), st, heads, d, 1, qq,
+             chunk_row=chunk if chunk > 0 else 64, **kw)
+    return y[0]
+
+
 def fuse(y, B: int, H: int, W: int, C: int, route_mask: int, scales):
     """Restored and fused output [B,H,W,C] in float64."""
     y = np.ascontiguousarray(y, dtype=np.float64)

@@ -1596,6 +1596,19 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
     return dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
 }
 
+srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
+                         const srnl_params *p, float *out)
+{
+    g_last_error.clear();
+    if (!p)
+        return fail(SRNL_ERR_PTR, "params is NULL");
+    srnl_params q = *p;
+    if (q.chunk_row == 0)
+        q.chunk_row = 64;   // the 1-D default chunk
+    q.chunk_col = 0;
+    return srnl_scan_fwd(x, B, 1, N, C, heads, d, 1u, &q, out);
+}
+
 srnl_status srnl_fuse(const float *y, int B, int H, int W, int C, unsigned route_mask,
                       const float *scales, srnl_dtype out_dtype, void *out, void *stream)
 {

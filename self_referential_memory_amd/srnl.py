@@ -21,7 +21,7 @@ SRNL_F32, SRNL_BF16 = 0, 1
 FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = (
     0x1, 0x2, 0x4, 0x8, 0x10)
 
-EXPORTS = ("srnl_scan_fwd", "srnl_fuse", "srnl_route_gather", "srnl_init_states",
+EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_route_gather", "srnl_init_states",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
            "srnl_last_error")
 
@@ -54,10 +54,12 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
         L.srnl_scan_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp]
+        L.srnl_scan_1d.argtypes = [vp, i, i, i, i, i, ctypes.POINTER(Params), vp]
         L.srnl_fuse.argtypes = [vp, i, i, i, i, u, vp, i, vp, vp]
         L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
         L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
-        for f in ("srnl_scan_fwd", "srnl_fuse", "srnl_route_gather", "srnl_init_states"):
+        for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_route_gather",
+                  "srnl_init_states"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
                                        ctypes.POINTER(i)]
@@ -112,6 +114,9 @@ def chunk_len(r: int, H: int, W: int, chunk_row: int = 0, chunk_col: int = 0) ->
 def make_params(states: torch.Tensor, x: torch.Tensor, q: Optional[torch.Tensor] = None, *,
                 alpha_max: float = 0.9, eps: float = 1e-6, chunk_row: int = 0,
                 chunk_col: int = 0, flags: int = 0, stream=None) -> Params:
+    if q is not None and (q.dtype != x.dtype or q.shape != x.shape):
+        raise SrnlError(SRNL_ERR_DTYPE, "make_params",
+                        "separate queries must have the shape and dtype of x")
     return Params(_ptr(states), _ptr(q), _dtype_code(x), alpha_max, eps, chunk_row,
                   chunk_col, flags, _stream(stream))
 
@@ -128,6 +133,19 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
     p = params if params is not None else make_params(states, x, q, **kw)
     _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
                                ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
+    return out
+
+
+def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
+            q: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, *,
+            chunk: int = 0, params: Optional[Params] = None, **kw) -> torch.Tensor:
+    """srnl_scan_1d: x [B,N,C] -> y [B,N,C] fp32 (chunk 0 selects 64 tokens)."""
+    B, N, C = x.shape
+    if out is None:
+        out = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
+    p = params if params is not None else make_params(states, x, q, chunk_row=chunk, **kw)
+    _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
+           "srnl_scan_1d")
     return out
 
 

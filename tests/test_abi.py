@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "srnl.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(srnl_[a-z_]+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(srnl_[a-z0-9_]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -113,3 +113,29 @@ def test_status_strings():
     L = srnl.lib()
     for s in (0, -1, -2, -3, -5):
         assert L.srnl_status_string(s).decode() not in ("", "unknown status")
+
+
+def _scan_1d(x=0, B=1, N=4, C=8, heads=2, d=4, **kw):
+    p = srnl.Params(None, None, kw.pop("in_dtype", 0), kw.pop("alpha_max", 0.9),
+                    kw.pop("eps", 1e-6), kw.pop("chunk_row", 0), 0, kw.pop("flags", 0), None)
+    return srnl.lib().srnl_scan_1d(x, B, N, C, heads, d, ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=12, C=24), srnl.SRNL_ERR_ARG),          # head dim not allowed
+    (dict(C=12), srnl.SRNL_ERR_ARG),                # C != heads * d
+    (dict(N=-1), srnl.SRNL_ERR_ARG),
+    (dict(B=-1), srnl.SRNL_ERR_ARG),
+    (dict(chunk_row=-3), srnl.SRNL_ERR_ARG),
+    (dict(alpha_max=1.0), srnl.SRNL_ERR_ARG),
+    (dict(in_dtype=7), srnl.SRNL_ERR_DTYPE),
+])
+def test_scan_1d_argument_errors(kw, status):
+    assert _scan_1d(**kw) == status
+
+
+def test_scan_1d_null_params_and_empty_sequence():
+    L = srnl.lib()
+    assert L.srnl_scan_1d(None, 1, 4, 8, 2, 4, None, None) == srnl.SRNL_ERR_PTR
+    assert _scan_1d(N=0) == srnl.SRNL_OK      # empty sequence: no-op, no pointer needed
+    assert _scan_1d(B=0) == srnl.SRNL_OK

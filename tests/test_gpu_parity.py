@@ -315,3 +315,86 @@ def test_empty_batch_launches_nothing():
     st = torch.zeros(4, 2, 56, device=DEV)
     y = srnl.scan_fwd(x, st, 2, 4, 15)
     assert y.shape == (4, 0, 9, 8)
+
+
+# ------------------------------------------------------------ standalone 1-D SRNL
+
+def _seq(B, N, C, heads, d, seed, dtype="f32", separate_q=False):
+    """Seeded [B][N][C] sequence, [heads][3d^2+2d] states and optional queries."""
+    x = synth.normals(seed, 1, B * N * C).reshape(B, N, C).astype(np.float32)
+    st = synth.states(seed, heads, d, 0.02)[0]          # [heads][3d^2+2d]
+    q = synth.normals(seed, 5, B * N * C).reshape(B, N, C).astype(np.float32) if separate_q else None
+    if dtype == "bf16":
+        x = synth.round_bf16(x)[0]
+        q = None if q is None else synth.round_bf16(q)[0]
+    return x, st, q
+
+
+def _scan_1d_gpu(x, st, heads, d, q=None, dtype="f32", chunk=0):
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"[gpu] scan_1d B={x.shape[0]} N={x.shape[1]} C={x.shape[2]} {heads}x{d} "
+          f"{dtype} chunk={chunk} q={q is not None}", flush=True)
+    xg = _dev(x, dt)
+    qg = None if q is None else _dev(q, dt)
+    y = srnl.scan_1d(xg, _dev(st, torch.float32), heads, d, qg, chunk=chunk)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [0, 100])
+def test_scan_1d_matches_oracle(d, dtype, chunk):
+    """README operator shape: [2, 257, 64], default 64-token chunks (short final
+    chunk of 1 token) and a 100-token override."""
+    B, N, C = 2, 257, 64
+    heads = C // d
+    x, st, _ = _seq(B, N, C, heads, d, seed=40 + d, dtype=dtype)
+    yg = _scan_1d_gpu(x, st, heads, d, dtype=dtype, chunk=chunk)
+    yo = oracle.scan_1d(x, st, heads, d, chunk=chunk)
+    assert np.isfinite(yg).all()
+    assert rel(yg, yo) <= TOL32, rel(yg, yo)
+    assert chunk_rel(yg, yo, chunk if chunk > 0 else 64) <= TOL_CHUNK
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 1000])
+def test_scan_1d_lengths(N):
+    B, C, heads, d = 3, 64, 2, 32
+    x, st, _ = _seq(B, N, C, heads, d, seed=N)
+    yg = _scan_1d_gpu(x, st, heads, d)
+    yo = oracle.scan_1d(x, st, heads, d)
+    assert rel(yg, yo) <= TOL32
+    assert chunk_rel(yg, yo, 64) <= TOL_CHUNK
+
+
+def test_scan_1d_separate_queries():
+    B, N, C, heads, d = 2, 300, 64, 2, 32
+    x, st, q = _seq(B, N, C, heads, d, seed=77, dtype="bf16", separate_q=True)
+    yg = _scan_1d_gpu(x, st, heads, d, q=q, dtype="bf16")
+    yo = oracle.scan_1d(x, st, heads, d, q=q)
+    assert rel(yg, yo) <= TOL32
+
+
+def test_scan_1d_equals_row_route_of_1xN_grid_bitwise():
+    B, N, C, heads, d = 2, 200, 64, 2, 32
+    x, st, _ = _seq(B, N, C, heads, d, seed=3, dtype="bf16")
+    y1 = _scan_1d_gpu(x, st, heads, d, dtype="bf16")
+    st4 = np.zeros((4,) + st.shape, np.float32)
+    st4[0] = st
+    xg = _dev(x.reshape(B, 1, N, C), torch.bfloat16)
+    y2 = srnl.scan_fwd(xg, _dev(st4, torch.float32), heads, d, 1, chunk_row=64)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2.double().cpu().numpy()[0])
+
+
+def test_scan_1d_query_dtype_must_match():
+    x = torch.zeros((1, 8, 64), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((1, 8, 64), dtype=torch.float32, device=DEV)
+    st = torch.zeros((2, srnl_state(32)), dtype=torch.float32, device=DEV)
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_1d(x, st, 2, 32, q)
+    assert e.value.status == srnl.SRNL_ERR_DTYPE
+
+
+def srnl_state(d):
+    return 3 * d * d + 2 * d

@@ -481,3 +481,28 @@ def test_oracle_rejects_bad_arguments():
             oracle.scan(x, st, 2, 4, rm, **kw)
     with pytest.raises(ValueError):   # C != heads * d
         oracle.scan(x, st, 3, 4, 15)
+
+
+# ------------------------------------------------------------ standalone 1-D SRNL
+
+def test_scan_1d_is_the_row_route_of_a_1xN_grid_brute_force():
+    """1-D SRNL [README SRNL and VisionHOPE operator] on 11 tokens, chunk 4 (a
+    short final chunk of 3), against the dense long-double brute force on the
+    1 x 11 grid's row-major route."""
+    d, heads = 4, 2
+    x, st = _wl(1, 11, d=d, heads=heads, seed=21, std=0.5, B=2)
+    y = oracle.scan_1d(x[:, 0], st[0], heads, d, chunk=4)
+    yb = brute_force(x, st, heads, d, 1, chunk_row=4).astype(np.float64)[0]
+    assert y.shape == (2, 11, heads * d)
+    assert np.abs(y - yb).max() <= 1e-12 * np.abs(yb).max()
+
+
+def test_scan_1d_default_chunk_is_64_tokens():
+    d, heads = 4, 1
+    x, st = _wl(1, 130, d=d, heads=heads, seed=22, std=0.5, B=1)
+    y0 = oracle.scan_1d(x[:, 0], st[0], heads, d)
+    y64 = oracle.scan_1d(x[:, 0], st[0], heads, d, chunk=64)
+    yN = oracle.scan_1d(x[:, 0], st[0], heads, d, chunk=130)
+    assert np.array_equal(y0, y64)
+    assert not np.allclose(y0[:, 64:], yN[:, 64:], rtol=1e-6, atol=0)
+    assert np.array_equal(y0[:, :64], yN[:, :64])   # the first chunk is the same
