@@ -43,6 +43,7 @@ typedef enum {
     SRNL_ERR_ARG = -1,       /* a size, mask, head_dim or scalar is invalid */
     SRNL_ERR_DTYPE = -2,     /* unknown dtype */
     SRNL_ERR_PTR = -3,       /* NULL, or not device memory where required */
+    SRNL_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
     SRNL_ERR_HIP = -5        /* a HIP runtime call or launch failed */
 } srnl_status;
 
@@ -161,6 +162,54 @@ srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
 srnl_status srnl_fuse(const float *y_routes, int B, int H, int W, int C,
                       unsigned route_mask, const float *scales,
                       srnl_dtype out_dtype, void *out, void *stream);
+
+/*
+ * Backward pass [README SRNL and VisionHOPE operator: the operator supports
+ * training with autograd]. The gradients are those of the forward pass
+ * above, in the same readings and variants (params are the forward's).
+ *
+ * srnl_scan_bwd_workspace_bytes -- bytes of device workspace srnl_scan_bwd
+ * needs for these sizes (0 for an empty grid).
+ *
+ * srnl_scan_bwd -- given dy = dL/dy for the scan outputs, computes
+ *   dx      [B][H][W][C] fp32 = dL/dx (overwritten; includes the query
+ *           path when params->q is NULL, i.e. q = x);
+ *   dq      [B][H][W][C] fp32 = dL/dq when params->q is not NULL
+ *           (overwritten), else unused and may be NULL;
+ *   dstates [4][heads][3d^2+2d] fp32 = dL/d(initial states), summed over
+ *           the batch (overwritten; zero for inactive routes).
+ *   dy      [R][B][H*W][C] fp32 in the layout srnl_scan_fwd writes.
+ * Per chain it re-runs the forward to record the boundary of every chunk,
+ * then walks the chunks backwards, re-running each chunk to record the
+ * working state after every token, and walks the tokens backwards.
+ * The workspace is caller-owned device memory of at least
+ * srnl_scan_bwd_workspace_bytes(...) bytes; its contents are scratch.
+ * Errors: as srnl_scan_fwd, plus SRNL_ERR_WORKSPACE, and SRNL_ERR_PTR for
+ * missing dy, dx, dstates or (with separate queries) dq.
+ */
+size_t srnl_scan_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                     unsigned route_mask, const srnl_params *params);
+srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                          unsigned route_mask, const srnl_params *params,
+                          const float *dy, void *workspace, size_t workspace_bytes,
+                          float *dx, float *dq, float *dstates);
+
+/*
+ * srnl_fuse_bwd_workspace_bytes / srnl_fuse_bwd -- backward of srnl_fuse:
+ *   dy_routes[slot(r)][b][t][c] = scales[r][c] * dout[b][i][j][c] with
+ *     (i, j) the cell route r visits at step t  (overwritten);
+ *   dscales[r][c] = sum over b, t of y_routes[slot(r)][b][t][c] *
+ *     dout[b][i][j][c]  (overwritten; zero rows for inactive routes).
+ *   dout [B][H][W][C] fp32; y_routes, dy_routes [R][B][H*W][C] fp32;
+ *   scales, dscales [4][C] fp32. Sums run in a fixed order (bitwise
+ *   reproducible). Errors: SRNL_ERR_ARG, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE,
+ *   SRNL_ERR_HIP.
+ */
+size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_mask);
+srnl_status srnl_fuse_bwd(const float *dout, const float *y_routes, int B, int H, int W,
+                          int C, unsigned route_mask, const float *scales,
+                          float *dy_routes, float *dscales, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * srnl_route_gather -- the route traversal as a standalone copy [OVERVIEW

@@ -1398,6 +1398,10 @@ __global__ __launch_bounds__(256) void init_kernel(float *__restrict__ st, long 
     }
 }
 
+// ------------------------------------------------------------ backward pass
+
+#include "srnl_bwd.inc"
+
 // ------------------------------------------------------------ host side
 
 bool valid_d(int d) { return d == 4 || d == 8 || d == 16 || d == 32 || d == 64; }
@@ -1521,6 +1525,127 @@ srnl_status check_grid(int B, int H, int W, int C, unsigned mask, long long *n_o
     return SRNL_OK;
 }
 
+// Workspace layout of srnl_scan_bwd (floats, 64-float aligned parts):
+// per-chain scratch, per-route dx partials, per-route dq partials, per-chain
+// initial-state gradients.
+struct BwdLayout {
+    long long chain_floats = 0, chains = 0, o_dx = 0, o_dq = 0, o_st = 0, total = 0;
+};
+
+long long align64(long long n) { return (n + 63) / 64 * 64; }
+
+BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask,
+                     const srnl_params *p)
+{
+    BwdLayout l;
+    const int R = popcount4(mask);
+    const long long N = static_cast<long long>(H) * W;
+    const long long rows = 3LL * d + 2;
+    for (int r = 0; r < 4; ++r) {
+        if (!(mask & (1u << r)))
+            continue;
+        long long L = (r < 2) ? (p->chunk_row > 0 ? p->chunk_row : W)
+                              : (p->chunk_col > 0 ? p->chunk_col : H);
+        if (L > N)
+            L = N;
+        if (L < 1)
+            L = 1;
+        const long long nch = (N + L - 1) / L;
+        const long long f = nch * rows * d + L * d * d + rows * d;
+        if (f > l.chain_floats)
+            l.chain_floats = f;
+    }
+    l.chain_floats = align64(l.chain_floats);
+    l.chains = static_cast<long long>(R) * B * heads;
+    const long long part = align64(static_cast<long long>(R) * B * N * C);
+    l.o_dx = l.chains * l.chain_floats;
+    l.o_dq = l.o_dx + part;
+    l.o_st = l.o_dq + (p->q ? part : 0);
+    l.total = l.o_st + align64(l.chains * rows * d);
+    return l;
+}
+
+template <int D, typename InT>
+srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
+                            int heads, unsigned mask, const float *dy, float *ws,
+                            const BwdLayout &l, float *dx, float *dq, float *dstates)
+{
+    const int R = popcount4(mask);
+    const int nchains = static_cast<int>(l.chains);
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    float *dxr = ws + l.o_dx, *dqr = p->q ? ws + l.o_dq : nullptr, *dstp = ws + l.o_st;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(nchains), dim3(BwdCfg<D>::NT), 0, st,
+                           static_cast<const InT *>(x), static_cast<const InT *>(p->q), p->states,
+                           dy, ws, l.chain_floats, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                           p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
+    };
+    if (p->flags & F_READ_BEFORE)
+        go(scan_bwd_kernel<D, true, InT>);
+    else
+        go(scan_bwd_kernel<D, false, InT>);
+    srnl_status s = launch_check("scan_bwd_kernel");
+    if (s != SRNL_OK)
+        return s;
+    const long long n = static_cast<long long>(B) * H * W * C;
+    hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dxr, dx, R, n);
+    if (p->q)
+        hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dqr, dq, R, n);
+    const int sz = 3 * D * D + 2 * D;
+    hipLaunchKernelGGL(states_grad_kernel, dim3(grid_for(4LL * heads * sz, 256)), dim3(256), 0, st,
+                       dstp, dstates, B, heads, R, mask, sz);
+    return launch_check("scan_bwd reductions");
+}
+
+template <typename InT>
+srnl_status dispatch_scan_bwd(int d, const void *x, const srnl_params *p, int B, int H, int W,
+                              int C, int heads, unsigned mask, const float *dy, float *ws,
+                              const BwdLayout &l, float *dx, float *dq, float *dstates)
+{
+    switch (d) {
+    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    }
+    return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
+}
+
+constexpr long long kFuseBwdRows = 2048;   // rows per partial-sum block of srnl_fuse_bwd
+
+long long fuse_bwd_blocks(int B, int H, int W)
+{
+    const long long rows = static_cast<long long>(B) * H * W;
+    return (rows + kFuseBwdRows - 1) / kFuseBwdRows;
+}
+
+// validation shared by the forward and the backward scan
+srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsigned route_mask,
+                            const srnl_params *p, long long *n)
+{
+    if (!p)
+        return fail(SRNL_ERR_PTR, "params is NULL");
+    if (!valid_d(d))
+        return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
+    if (heads < 1 || C != heads * d)
+        return fail(SRNL_ERR_ARG, "C must equal heads * d with heads >= 1");
+    srnl_status s = check_grid(B, H, W, C, route_mask, n);
+    if (s != SRNL_OK)
+        return s;
+    if (!(p->alpha_max > 0.0f && p->alpha_max < 1.0f))
+        return fail(SRNL_ERR_ARG, "alpha_max must lie in (0, 1)");
+    if (!(p->eps > 0.0f) || !std::isfinite(p->eps))
+        return fail(SRNL_ERR_ARG, "eps must be positive and finite");
+    if (p->chunk_row < 0 || p->chunk_col < 0)
+        return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
+    if (p->flags & ~0x1Fu)
+        return fail(SRNL_ERR_ARG, "unknown flag bits");
+    if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
+        return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
+    return SRNL_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI
@@ -1534,6 +1659,7 @@ const char *srnl_status_string(srnl_status s)
     case SRNL_ERR_ARG: return "invalid argument";
     case SRNL_ERR_DTYPE: return "invalid dtype";
     case SRNL_ERR_PTR: return "invalid pointer";
+    case SRNL_ERR_WORKSPACE: return "workspace too small";
     case SRNL_ERR_HIP: return "HIP error";
     }
     return "unknown status";
@@ -1633,6 +1759,85 @@ srnl_status srnl_fuse(const float *y, int B, int H, int W, int C, unsigned route
         hipLaunchKernelGGL(fuse_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, y, scales,
                            static_cast<uint16_t *>(out), B, H, W, C, route_mask, nvec);
     return launch_check("fuse_kernel");
+}
+
+size_t srnl_scan_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                     unsigned route_mask, const srnl_params *p)
+{
+    long long n = 0;
+    if (check_scan_args(B, H, W, C, heads, d, route_mask, p, &n) != SRNL_OK || n == 0)
+        return 0;
+    return static_cast<size_t>(bwd_layout(B, H, W, C, heads, d, route_mask, p).total) * sizeof(float);
+}
+
+srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                          unsigned route_mask, const srnl_params *p, const float *dy,
+                          void *workspace, size_t workspace_bytes, float *dx, float *dq,
+                          float *dstates)
+{
+    g_last_error.clear();
+    long long n = 0;
+    srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
+    if (s != SRNL_OK)
+        return s;
+    if (n == 0)
+        return SRNL_OK;   // empty grid
+    const BwdLayout l = bwd_layout(B, H, W, C, heads, d, route_mask, p);
+    if (!workspace || workspace_bytes < static_cast<size_t>(l.total) * sizeof(float))
+        return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_scan_bwd_workspace_bytes");
+    if (!is_device_ptr(x) || !is_device_ptr(p->states) || !is_device_ptr(dy) ||
+        !is_device_ptr(dx) || !is_device_ptr(dstates) || !is_device_ptr(workspace))
+        return fail(SRNL_ERR_PTR, "x, states, dy, dx, dstates and workspace must be device memory");
+    if (p->q && (!is_device_ptr(p->q) || !is_device_ptr(dq)))
+        return fail(SRNL_ERR_PTR, "with separate queries, q and dq must be device memory");
+    if (l.chains > INT_MAX)
+        return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
+    float *ws = static_cast<float *>(workspace);
+    if (p->in_dtype == SRNL_F32)
+        return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq, dstates);
+    return dispatch_scan_bwd<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq, dstates);
+}
+
+size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_mask)
+{
+    long long n = 0;
+    if (check_grid(B, H, W, C, route_mask, &n) != SRNL_OK || n == 0)
+        return 0;
+    return static_cast<size_t>(popcount4(route_mask) * fuse_bwd_blocks(B, H, W) * C) * sizeof(float);
+}
+
+srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W, int C,
+                          unsigned route_mask, const float *scales, float *dyr, float *dscales,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    long long n = 0;
+    srnl_status s = check_grid(B, H, W, C, route_mask, &n);
+    if (s != SRNL_OK)
+        return s;
+    if (C > 1024)
+        return fail(SRNL_ERR_ARG, "srnl_fuse_bwd supports C <= 1024");
+    if (n == 0)
+        return SRNL_OK;
+    const int R = popcount4(route_mask);
+    const long long nblk = fuse_bwd_blocks(B, H, W);
+    if (!workspace || workspace_bytes < static_cast<size_t>(R * nblk * C) * sizeof(float))
+        return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_fuse_bwd_workspace_bytes");
+    if (nblk > 65535LL * 16)
+        return fail(SRNL_ERR_ARG, "grid too large for srnl_fuse_bwd");
+    if (!is_device_ptr(dout) || !is_device_ptr(y) || !is_device_ptr(scales) ||
+        !is_device_ptr(dyr) || !is_device_ptr(dscales) || !is_device_ptr(workspace))
+        return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be device memory");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *part = static_cast<float *>(workspace);
+    hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk), R), dim3(256), 0, st, dout, y,
+                       scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
+    s = launch_check("fuse_bwd_kernel");
+    if (s != SRNL_OK)
+        return s;
+    hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C, 256)), dim3(256), 0, st, part,
+                       dscales, C, route_mask, static_cast<int>(nblk));
+    return launch_check("fuse_bwd_scales_kernel");
 }
 
 srnl_status srnl_route_gather(const void *x, int B, int H, int W, int C, unsigned route_mask,

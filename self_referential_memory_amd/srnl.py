@@ -16,12 +16,15 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsrnl.so")
 
-SRNL_OK, SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_HIP = 0, -1, -2, -3, -5
+SRNL_OK, SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE, SRNL_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
 SRNL_F32, SRNL_BF16 = 0, 1
 FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = (
     0x1, 0x2, 0x4, 0x8, 0x10)
 
-EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_route_gather", "srnl_init_states",
+EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
+           "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
+           "srnl_route_gather", "srnl_init_states",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
            "srnl_last_error")
 
@@ -56,10 +59,18 @@ def lib() -> ctypes.CDLL:
         L.srnl_scan_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp]
         L.srnl_scan_1d.argtypes = [vp, i, i, i, i, i, ctypes.POINTER(Params), vp]
         L.srnl_fuse.argtypes = [vp, i, i, i, i, u, vp, i, vp, vp]
+        sz = ctypes.c_size_t
+        L.srnl_scan_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, u, ctypes.POINTER(Params)]
+        L.srnl_scan_bwd_workspace_bytes.restype = sz
+        L.srnl_scan_bwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp, vp, sz,
+                                    vp, vp, vp]
+        L.srnl_fuse_bwd_workspace_bytes.argtypes = [i, i, i, i, u]
+        L.srnl_fuse_bwd_workspace_bytes.restype = sz
+        L.srnl_fuse_bwd.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp, sz, vp]
         L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
         L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
-        for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_route_gather",
-                  "srnl_init_states"):
+        for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd", "srnl_fuse_bwd",
+                  "srnl_route_gather", "srnl_init_states"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
                                        ctypes.POINTER(i)]
@@ -158,6 +169,37 @@ def fuse(y: torch.Tensor, B: int, H: int, W: int, C: int, route_mask: int,
     _check(lib().srnl_fuse(_ptr(y), B, H, W, C, route_mask, _ptr(scales),
                            _dtype_code(out), _ptr(out), _stream(stream)), "srnl_fuse")
     return out
+
+
+def scan_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torch.Tensor,
+             route_mask: int = 15, q: Optional[torch.Tensor] = None, *,
+             params: Optional[Params] = None, **kw):
+    """srnl_scan_bwd: dy [R,B,H*W,C] fp32 -> (dx [B,H,W,C], dq or None, dstates
+    [4,heads,3d^2+2d]), all fp32. The workspace is allocated here (torch)."""
+    B, H, W, C = x.shape
+    p = params if params is not None else make_params(states, x, q, **kw)
+    nbytes = lib().srnl_scan_bwd_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
+    dx = torch.empty((B, H, W, C), dtype=torch.float32, device=x.device)
+    dq = None if q is None else torch.empty_like(dx)
+    dst = torch.empty((4, heads, 3 * d * d + 2 * d), dtype=torch.float32, device=x.device)
+    _check(lib().srnl_scan_bwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
+                               _ptr(dy), _ptr(ws), int(nbytes), _ptr(dx), _ptr(dq), _ptr(dst)),
+           "srnl_scan_bwd")
+    return dx, dq, dst
+
+
+def fuse_bwd(dout: torch.Tensor, y: torch.Tensor, B: int, H: int, W: int, C: int,
+             route_mask: int, scales: torch.Tensor, stream=None):
+    """srnl_fuse_bwd: dout [B,H,W,C] fp32 -> (dy_routes [R,B,H*W,C], dscales [4,C])."""
+    nbytes = lib().srnl_fuse_bwd_workspace_bytes(B, H, W, C, route_mask)
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dout.device)
+    dyr = torch.empty_like(y)
+    dsc = torch.empty((4, C), dtype=torch.float32, device=dout.device)
+    _check(lib().srnl_fuse_bwd(_ptr(dout), _ptr(y), B, H, W, C, route_mask, _ptr(scales),
+                               _ptr(dyr), _ptr(dsc), _ptr(ws), int(nbytes), _stream(stream)),
+           "srnl_fuse_bwd")
+    return dyr, dsc
 
 
 def route_gather(x: torch.Tensor, route_mask: int = 15, out: Optional[torch.Tensor] = None,

@@ -1,0 +1,139 @@
+"""GPU parity of the backward pass: srnl_scan_bwd and srnl_fuse_bwd (through
+the C ABI) against the reference gradients of oracle/srnl_grad.py on the same
+seeded inputs.
+
+Bar: max |gpu - ref| / max |ref| <= 1e-3 for every gradient (dx, dq, the
+initial states, the scales). The gradient runs the fp32 recurrence backwards
+through every token of the chain, so it is a longer fp32 computation than
+the forward (whose bar is 1e-4).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import srnl_grad as G
+from self_referential_memory_amd import srnl, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-3
+
+_CAP = {0: G.CAP_SOFT, srnl.FLAG_HARD_CAP: G.CAP_HARD, srnl.FLAG_NO_CAP: G.CAP_OFF}
+
+
+def _kw(wl, flags):
+    return dict(alpha_max=wl.alpha_max, eps=wl.eps, chunk_row=wl.chunk_row,
+                chunk_col=wl.chunk_col, cap_mode=_CAP[flags & 0x3],
+                clamp=not (flags & srnl.FLAG_NO_CLAMP),
+                fixed_alpha=bool(flags & srnl.FLAG_FIXED_ALPHA),
+                readout_before=bool(flags & srnl.FLAG_READ_BEFORE))
+
+
+def rel(g, o):
+    m = np.abs(o).max()
+    return float(np.abs(g - o).max() / m) if m > 0 else float(np.abs(g).max())
+
+
+def run_case(wl, mask=15, flags=0, seed=0):
+    """Full chain on the GPU: scan_fwd, fuse; then fuse_bwd and scan_bwd for
+    dL/dfused = dout, plus a direct dL/dy term; against autograd."""
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    R = bin(mask).count("1")
+    print(f"[gpu] grad {wl.name} B={wl.B} {wl.H}x{wl.W} C={wl.C} {wl.heads}x{wl.d} "
+          f"mask={mask} flags={flags} chunks=({wl.chunk_row},{wl.chunk_col}) "
+          f"q={wl.q is not None}", flush=True)
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((wl.B, wl.H, wl.W, wl.C)).astype(np.float32)
+    dyd = rng.standard_normal((R, wl.B, wl.N, wl.C)).astype(np.float32)
+    x = torch.from_numpy(wl.x).to(DEV).to(dt)
+    q = None if wl.q is None else torch.from_numpy(wl.q).to(DEV).to(dt)
+    st = torch.from_numpy(wl.states).to(DEV)
+    sc = torch.from_numpy(wl.scales).to(DEV)
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps, chunk_row=wl.chunk_row,
+              chunk_col=wl.chunk_col, flags=flags)
+    y = srnl.scan_fwd(x, st, wl.heads, wl.d, mask, q, **kw)
+    dyr, dsc = srnl.fuse_bwd(torch.from_numpy(dout).to(DEV), y, wl.B, wl.H, wl.W, wl.C, mask, sc)
+    dy = dyr + torch.from_numpy(dyd).to(DEV)
+    dx, dq, dst = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, mask, q, **kw)
+    torch.cuda.synchronize()
+    gx, gq, gst, gsc = G.grads(wl.x, wl.states, wl.scales, wl.heads, wl.d, mask, wl.q,
+                               dy=dyd, dfused=dout, **_kw(wl, flags))
+    got = dict(dx=dx.cpu().numpy(), dst=dst.cpu().numpy(), dsc=dsc.cpu().numpy())
+    ref = dict(dx=gx, dst=gst, dsc=gsc)
+    if wl.q is not None:
+        got["dq"], ref["dq"] = dq.cpu().numpy(), gq
+    for k in got:
+        assert np.isfinite(got[k]).all(), k
+        e = rel(got[k], ref[k])
+        assert e <= TOL, (k, e)
+    return got, ref
+
+
+def _wl(name, B, H, W, heads, d, dtype="f32", seed=1, **kw):
+    return synth.make(name, B, H, W, heads * d, heads, d, dtype, seed, **kw)
+
+
+@pytest.mark.parametrize("d,heads", [(4, 2), (8, 2), (16, 2), (32, 2), (64, 1)])
+def test_grad_head_dims(d, heads):
+    run_case(_wl(f"g{d}", 2, 5, 6, heads, d, seed=d, state_std=0.3))
+
+
+def test_grad_tiny_workload():
+    run_case(synth.tiny())
+
+
+@pytest.mark.parametrize("flags", [srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
+                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE])
+def test_grad_variants(flags):
+    std = 0.3 if flags == srnl.FLAG_NO_CAP else 1.0
+    run_case(_wl("gv", 2, 4, 5, 2, 16, seed=flags, state_std=std), flags=flags)
+
+
+def test_grad_stressed_inputs_cap_and_clamp_active():
+    run_case(_wl("gadv", 1, 6, 5, 2, 16, seed=9, state_std=3.0, outlier_frac=0.1))
+
+
+@pytest.mark.parametrize("cr,cc", [(3, 2), (1, 1), (7, 0), (100, 100)])
+def test_grad_chunk_overrides(cr, cc):
+    run_case(_wl("gch", 1, 5, 7, 2, 8, seed=cr * 10 + cc, state_std=0.5,
+                 chunk_row=cr, chunk_col=cc))
+
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 5, 10])
+def test_grad_route_masks(mask):
+    run_case(_wl("gm", 2, 4, 6, 1, 16, seed=mask), mask=mask)
+
+
+def test_grad_separate_queries_and_bf16():
+    run_case(_wl("gq", 2, 6, 6, 2, 32, dtype="bf16", seed=4, separate_q=True))
+
+
+def test_grad_d32_long_rows():
+    """A 6x40 map at d = 32: row chunks of 40 tokens span two sub-blocks of
+    the backward (32 + 8)."""
+    run_case(_wl("glong", 1, 6, 40, 2, 32, seed=6, x_kind="ar1"))
+
+
+def test_grad_is_deterministic():
+    wl = _wl("gdet", 2, 5, 5, 2, 16, seed=3)
+    a, _ = run_case(wl)
+    b, _ = run_case(wl)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_scan_bwd_workspace_errors():
+    x = torch.zeros((1, 2, 2, 8), device=DEV)
+    st = torch.zeros((4, 2, 3 * 16 + 8), device=DEV)
+    p = srnl.make_params(st, x)
+    n = srnl.lib().srnl_scan_bwd_workspace_bytes(1, 2, 2, 8, 2, 4, 15, p)
+    assert n > 0
+    dy = torch.zeros((4, 1, 4, 8), device=DEV)
+    dx = torch.empty_like(x)
+    dst = torch.empty_like(st)
+    ws = torch.empty(n - 4, dtype=torch.uint8, device=DEV)
+    import ctypes
+    rc = srnl.lib().srnl_scan_bwd(x.data_ptr(), 1, 2, 2, 8, 2, 4, 15, ctypes.byref(p),
+                                  dy.data_ptr(), ws.data_ptr(), n - 4, dx.data_ptr(), None,
+                                  dst.data_ptr())
+    assert rc == srnl.SRNL_ERR_WORKSPACE
