@@ -181,6 +181,83 @@ def main_seq1d(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_hier56_bwd(args):
+    """Backward of the hier56 step: srnl_fuse_bwd + srnl_scan_bwd for a given
+    dL/d(fused output), forward outputs and inputs resident in HBM."""
+    import numpy as np
+    import torch
+    from self_referential_memory_amd import srnl, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.hier56()
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(dev)
+    sc = torch.from_numpy(wl.scales).to(dev)
+    R = 4
+    y = srnl.scan_fwd(x, st, wl.heads, wl.d, 15)
+    dout = torch.from_numpy(np.random.default_rng(0).standard_normal(
+        (wl.B, wl.H, wl.W, wl.C)).astype(np.float32)).to(dev)
+    p = srnl.make_params(st, x)
+    L = srnl.lib()
+    import ctypes
+    nb_s = L.srnl_scan_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                           ctypes.byref(p))
+    nb_f = L.srnl_fuse_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, 15)
+    ws_s = torch.empty(nb_s, dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(nb_f, dtype=torch.uint8, device=dev)
+    dyr = torch.empty_like(y)
+    dsc = torch.empty((4, wl.C), dtype=torch.float32, device=dev)
+    dx = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(st)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(a=None, b=None):
+        L.srnl_fuse_bwd(dout.data_ptr(), y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15,
+                        sc.data_ptr(), dyr.data_ptr(), dsc.data_ptr(), ws_f.data_ptr(), nb_f, stream)
+        if a is not None:
+            a.record()
+        rc = L.srnl_scan_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                             ctypes.byref(p), dyr.data_ptr(), ws_s.data_ptr(), nb_s,
+                             dx.data_ptr(), None, dst.data_ptr())
+        if b is not None:
+            b.record()
+        if rc != 0:
+            raise RuntimeError(f"srnl_scan_bwd failed: {rc}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms = dt * 1000.0 / args.steps
+    units = wl.B * wl.H * wl.W * wl.heads
+    flops = 2 * algorithmic_flops_per_unit(wl.d) * units * R
+    achieved = flops / (scan_ms / 1000.0) / 1e12
+    rec = {
+        "metric": "SRNL bwd tokens·heads/s (4 routes) at stage shapes",
+        "value": units / (ms / 1000.0), "unit": "tokens·heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "hier56_bwd: backward of the hier56 step (srnl_fuse_bwd + "
+                               "srnl_scan_bwd), B=64, 56x56, C=64, 2 heads x d=32, 4 routes",
+                   "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads, "d": wl.d,
+                   "routes": R, "input_dtype": "bf16", "parallelism": "single GPU"},
+        "roofline": {"kernel": "scan_bwd_kernel", "bound": "alu", "achieved": achieved,
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,9 +271,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="digest two rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
-    ap.add_argument("--workload", choices=("hier56", "seq1d"), default="hier56",
+    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd"), default="hier56",
                     help="hier56: the 2-D four-route operator (default); seq1d: the "
-                         "standalone 1-D SRNL")
+                         "standalone 1-D SRNL; hier56_bwd: its backward pass")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_command)
@@ -208,6 +285,9 @@ def main():
         sys.exit(2)
     if args.workload == "seq1d":
         main_seq1d(args)
+        return
+    if args.workload == "hier56_bwd":
+        main_hier56_bwd(args)
         return
 
     import numpy as np

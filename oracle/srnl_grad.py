@@ -96,16 +96,25 @@ def forward(x, states, scales, heads: int, d: int, route_mask: int = 15, q=None,
         g = torch.where(pg > 0, torch.sqrt(torch.where(pg > 0, pg, torch.ones_like(pg))),
                         torch.zeros_like(pg))
         m = 1.0 - alpha
-        gs = torch.where(g > 0, g, torch.ones_like(g))   # safe divisor
+        one = torch.ones_like(g)
         if cap_mode == CAP_SOFT:
-            eta1 = torch.where(g > 0, m * torch.tanh(eta * g / m) / gs, eta)
+            # (1 - alpha) tanh(u) / g with u = eta g / (1 - alpha) is eta tanh(u) / u;
+            # written so, with tanh(u)/u's series below u = 1e-4 (its next term
+            # is below 1e-25), the derivative has no 1/g^2 cancellation on
+            # tiny g; u = 0 (g = 0) gives eta' = eta
+            u = eta * g / m
+            big = u > 1e-4
+            us = torch.where(big, u, one)
+            eta1 = eta * torch.where(big, torch.tanh(us) / us,
+                                     1.0 - u * u / 3.0 + 2.0 * u ** 4 / 15.0)
         elif cap_mode == CAP_HARD:
-            eta1 = torch.where((g > 0) & (m / gs < eta), m / gs, eta)
+            act = (g > 0) & (m < eta * g)
+            eta1 = torch.where(act, m / torch.where(act, g, one), eta)
         else:
             eta1 = eta
         if clamp:
-            ns = torch.where(nkh2 > 0, nkh2, torch.ones_like(nkh2))
-            eta2 = torch.where(nkh2 > 0, torch.minimum(eta1, 2.0 * alpha / ns), eta1)
+            act = (nkh2 > 0) & (2.0 * alpha < eta1 * nkh2)   # 2 alpha / |k^|^2 < eta'
+            eta2 = torch.where(act, 2.0 * alpha / torch.where(act, nkh2, one), eta1)
         else:
             eta2 = eta1
         qt = Q[:, :, t]

@@ -137,3 +137,9 @@ def test_scan_bwd_workspace_errors():
                                   dy.data_ptr(), ws.data_ptr(), n - 4, dx.data_ptr(), None,
                                   dst.data_ptr())
     assert rc == srnl.SRNL_ERR_WORKSPACE
+
+
+def test_grad_hier56_full_map():
+    """The benchmark's map at full size (56x56, C=64, 2 heads x d=32, four
+    routes, AR(1) rows, bf16 input) on two batch items."""
+    run_case(synth.make("hier56_b2", 2, 56, 56, 64, 2, 32, "bf16", 2, x_kind="ar1"))
