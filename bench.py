@@ -26,14 +26,34 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SRNL fwd tokens·heads/s (4 routes) at stage shapes; % of HBM/MFMA roofline"
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "scan_kernel_hier56_traffic.json")
+COUNTERS_FILE = os.path.join(PROFILES, "hier56_pmc_counters.json")
 SRC = os.path.join(ROOT, "self_referential_memory_amd", "csrc", "srnl.hip")
 
-# Published MI355X peaks used for the roofline (dense fp32 MFMA; the fp32
-# vector peak is the same figure).
+# Published MI355X peaks used for the rooflines (dense MFMA fp32 and bf16; the
+# fp32 vector peak is the same figure as the fp32 MFMA one).
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+COPY_PROBE_BYTES = 1 << 30      # one plain device-to-device copy of 1 GiB ...
+COPY_PROBE_REPS = 3             # ... done this many times after the timed steps
+
+# Counter passes over this script (one rocprofv3 --pmc run each, with
+# --steps 3 --warmup 1 --no-cpu-baseline --copy-probe), digested by
+# --pmc-summary into COUNTERS_FILE.
+PMC_PASSES = (
+    ("fetch", ("FETCH_SIZE",)),
+    ("write", ("WRITE_SIZE",)),
+    ("tcc_rd", ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                "TCC_EA0_RDREQ_128B_sum")),
+    ("tcc_wr", ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")),
+    ("mfma", ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")),
+    ("insts", ("SQ_INSTS_VALU_MFMA_F32", "SQ_INSTS_VALU_MFMA_BF16", "SQ_LDS_BANK_CONFLICT",
+               "SQ_LDS_IDX_ACTIVE")),
+)
+KERNEL_KEYS = (("scan_kernel", "scan_mfma_kernel<32"), ("fuse_kernel", "fuse_kernel"),
+               ("gather_kernel", "gather_kernel"))
 
 
 def algorithmic_flops_per_unit(d: int) -> int:
@@ -44,53 +64,119 @@ def algorithmic_flops_per_unit(d: int) -> int:
     return (10 * d * d + 8 * d) + (17 * d * d + 20 * d)
 
 
+def algorithmic_bytes(wl, R: int) -> dict:
+    """Bytes each kernel of the step must move at least, bf16 input: the scan
+    reads x once per route and writes the fp32 route outputs; the fuse reads
+    those and writes the bf16 map; the gather reads x and writes R bf16
+    copies in route order."""
+    n = wl.B * wl.H * wl.W * wl.C
+    st = 4 * wl.heads * (3 * wl.d * wl.d + 2 * wl.d) * 4
+    return {"scan_kernel": R * n * 2 + st + R * n * 4,
+            "fuse_kernel": R * n * 4 + R * wl.C * 4 + n * 2,
+            "gather_kernel": n * 2 + R * n * 2}
+
+
 def src_sha() -> str:
     return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(launches_units: int):
-    """HBM bytes per scan launch from the committed PMC summary, if it was
-    taken on the current kernel source; else None."""
+def load_counters():
+    """The committed counter digest, if it was taken on the current kernel
+    source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != src_sha():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("kernel_source_sha") == src_sha() else None
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, command: str) -> None:
-    """Digest two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of this
-    script with --copy-probe) into profiles/scan_kernel_hier56_traffic.json:
-    per-dispatch counter averages, calibrated against the plain 1 GiB device
-    copy the probe runs (1 GiB read and 1 GiB written per dispatch)."""
-    import csv
+def pmc_summary(root: str, command: str) -> None:
+    """Digest the rocprofv3 runs under root (one directory per PMC_PASSES
+    entry holding run_counter_collection.csv, plus ktrace/run_kernel_stats.csv
+    from a --kernel-trace --stats run) into COUNTERS_FILE.
+
+    HBM bytes: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    same counter reads for the copy probe (the sum over all copy dispatches
+    against COPY_PROBE_REPS x 1 GiB each way); cross-checked against the raw
+    TCC-to-memory request counts by size (32, 64, 128 B reads; 32, 64 B
+    writes). MFMA: SQ_INSTS_VALU_MFMA_MOPS_* count MFMA work in units of 512
+    flops; utilisation is that work at the published dense peak of its type,
+    over the kernel's average duration."""
     import collections
+    import csv
 
-    def read(path, counter):
-        agg = collections.defaultdict(list)
+    def read(name):
+        path = os.path.join(root, name, "run_counter_collection.csv")
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
-                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in agg.items()}
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return agg
 
-    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
-    pick = lambda d, key: next(v for k, v in d.items() if key in k)
-    gib = float(1 << 30)
-    f_scale = gib / (pick(fetch, "copyBuffer") * 1024.0)
-    w_scale = gib / (pick(write, "copyBuffer") * 1024.0)
+    def per_kernel(agg, key):
+        rows = [v for k, v in agg.items() if key in k]
+        if not rows:
+            return None
+        return {c: sum(x) / len(x) for c, x in rows[0].items()}
+
+    def total(agg, key, counter):
+        return sum(sum(v[counter]) for k, v in agg.items() if key in k)
+
+    passes = {name: read(name) for name, _ in PMC_PASSES}
+    stats = {}
+    with open(os.path.join(root, "ktrace", "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            stats[r["Name"]] = r
+    dur = {}
+    for name, key in KERNEL_KEYS:
+        row = next((v for k, v in stats.items() if key in k), None)
+        dur[name] = None if row is None else float(row["AverageNs"]) * 1e-9
+    probe = COPY_PROBE_BYTES * COPY_PROBE_REPS
+    f_scale = probe / (total(passes["fetch"], "copyBuffer", "FETCH_SIZE") * 1024.0)
+    w_scale = probe / (total(passes["write"], "copyBuffer", "WRITE_SIZE") * 1024.0)
     out = {"kernel_source_sha": src_sha(), "command": command,
-           "copy_probe": {"bytes_each_way": int(gib), "fetch_scale": f_scale,
+           "copy_probe": {"bytes_each_way": probe, "fetch_scale": f_scale,
                           "write_scale": w_scale}}
-    for key, name in (("scan_mfma_kernel<32", "scan_kernel"), ("fuse_kernel", "fuse_kernel")):
-        fb = pick(fetch, key) * 1024.0 * f_scale
-        wb = pick(write, key) * 1024.0 * w_scale
-        out[name] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                     "hbm_bytes_per_launch": fb + wb}
+    for name, key in KERNEL_KEYS:
+        F = per_kernel(passes["fetch"], key)
+        if F is None:
+            continue
+        Wr = per_kernel(passes["write"], key)
+        rd = per_kernel(passes["tcc_rd"], key)
+        wr = per_kernel(passes["tcc_wr"], key)
+        fb = F["FETCH_SIZE"] * 1024.0 * f_scale
+        wb = Wr["WRITE_SIZE"] * 1024.0 * w_scale
+        k = {"average_duration_s": dur[name],
+             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+             "hbm_bytes_per_launch": fb + wb,
+             "raw": {"FETCH_SIZE_KiB": F["FETCH_SIZE"], "WRITE_SIZE_KiB": Wr["WRITE_SIZE"]}}
+        if rd is not None and wr is not None:
+            n32, n64 = rd["TCC_EA0_RDREQ_32B_sum"], rd["TCC_EA0_RDREQ_64B_sum"]
+            n128, nrd = rd["TCC_EA0_RDREQ_128B_sum"], rd["TCC_EA0_RDREQ_sum"]
+            w64, nwr = wr["TCC_EA0_WRREQ_64B_sum"], wr["TCC_EA0_WRREQ_sum"]
+            k["request_bytes"] = {"read": 32 * n32 + 64 * n64 + 128 * n128,
+                                  "write": 64 * w64 + 32 * (nwr - w64)}
+            k["raw"].update({"rd_req": nrd, "rd_32B": n32, "rd_64B": n64, "rd_128B": n128,
+                             "wr_req": nwr, "wr_64B": w64})
+        if dur[name]:
+            k["hbm_GBs"] = (fb + wb) / dur[name] / 1e9
+        m = per_kernel(passes["mfma"], key)
+        extra = per_kernel(passes["insts"], key)
+        if m is not None and extra is not None:
+            m = dict(m, **extra)
+        if m is not None and dur[name]:
+            f32 = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_F32"]
+            bf16 = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+            t = dur[name]
+            k["mfma"] = {
+                "f32_flops": f32, "bf16_flops": bf16,
+                "f32_TFLOPs": f32 / t / 1e12, "bf16_TFLOPs": bf16 / t / 1e12,
+                "pipe_util": (f32 / (PEAK_FP32_MFMA_TFLOPS * 1e12)
+                              + bf16 / (PEAK_BF16_MFMA_TFLOPS * 1e12)) / t,
+                "raw": m}
+        out[name] = k
     out["hbm_bytes_per_launch"] = out["scan_kernel"]["hbm_bytes_per_launch"]
     os.makedirs(PROFILES, exist_ok=True)
-    json.dump(out, open(TRAFFIC_FILE, "w"), indent=2)
+    json.dump(out, open(COUNTERS_FILE, "w"), indent=2)
     print(json.dumps(out, indent=2))
 
 
@@ -269,15 +355,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (PMC calibration)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="digest two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="digest the rocprofv3 runs under DIR (one directory per counter "
+                         "pass, plus ktrace/) into the committed counter summary")
+    ap.add_argument("--pmc-passes", action="store_true",
+                    help="print the counter passes, one line each: NAME COUNTER...")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
     ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd"), default="hier56",
                     help="hier56: the 2-D four-route operator (default); seq1d: the "
                          "standalone 1-D SRNL; hier56_bwd: its backward pass")
     args = ap.parse_args()
+    if args.pmc_passes:
+        for name, counters in PMC_PASSES:
+            print(name, " ".join(counters))
+        return
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_command)
+        pmc_summary(args.pmc_summary, args.pmc_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -306,32 +399,49 @@ def main():
     out = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.bfloat16, device=dev)
     p = srnl.make_params(st, x, alpha_max=wl.alpha_max, eps=wl.eps)
 
-    def step(ev_a=None, ev_b=None):
-        if ev_a is not None:
-            ev_a.record()
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
         srnl.scan_fwd(x, st, wl.heads, wl.d, 15, out=y, params=p)
-        if ev_b is not None:
-            ev_b.record()
+        if ev is not None:
+            ev[1].record()
         srnl.fuse(y, wl.B, wl.H, wl.W, wl.C, 15, sc, out=out)
+        if ev is not None:
+            ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
-        step(a, b)
+    for ev in evs:
+        step(ev)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    fuse_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    # the standalone route gather (not part of the step: the scan gathers its
+    # own tokens), timed after the steps for its bandwidth
+    g = torch.empty((R, wl.B, wl.N, wl.C), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        srnl.route_gather(x, 15, out=g)
+    gev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(10)]
+    for a, b in gev:
+        a.record()
+        srnl.route_gather(x, 15, out=g)
+        b.record()
+    torch.cuda.synchronize()
+    gather_ms = sum(a.elapsed_time(b) for a, b in gev) / len(gev)
+    del g
 
     if args.copy_probe:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(COPY_PROBE_REPS):
             dst.copy_(src)
         torch.cuda.synchronize()
 
@@ -341,7 +451,21 @@ def main():
     thr_units = units * R                            # tokens x heads x routes per launch
     flops = algorithmic_flops_per_unit(wl.d) * thr_units
     achieved = flops / (scan_ms / 1000.0) / 1e12
-    traffic = traffic_from_profile(thr_units)
+    prof = load_counters()
+    abytes = algorithmic_bytes(wl, R)
+    kernels = {}
+    for name, k_ms in (("scan_kernel", scan_ms), ("fuse_kernel", fuse_ms),
+                       ("gather_kernel", gather_ms)):
+        gbs = abytes[name] / (k_ms / 1000.0) / 1e9
+        e = {"us": k_ms * 1000.0, "algorithmic_bytes": abytes[name], "achieved_GBs": gbs,
+             "peak_GBs": PEAK_HBM_GBS, "hbm_frac": gbs / PEAK_HBM_GBS,
+             "pmc_hbm_bytes": None}
+        if prof is not None and name in prof:
+            e["pmc_hbm_bytes"] = prof[name]["hbm_bytes_per_launch"]
+            if "mfma" in prof[name]:
+                e["mfma_pipe_util"] = prof[name]["mfma"]["pipe_util"]
+                e["mfma_bf16_TFLOPs_generation"] = prof[name]["mfma"]["bf16_TFLOPs"]
+        kernels[name] = e
     rec = {
         "metric": METRIC,
         "value": value,
@@ -370,10 +494,11 @@ def main():
             "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-            "traffic": traffic,
+            "traffic": None if prof is None else prof["hbm_bytes_per_launch"],
             "scan_ms": scan_ms,
             "algorithmic_flops_per_launch": flops,
         },
+        "kernels": kernels,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -1272,8 +1272,6 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 
 // ------------------------------------------------------------ fuse kernel
 
-struct bf16x4 { uint16_t v[4]; };
-
 __device__ __forceinline__ void store4(float *o, float4 a) { *reinterpret_cast<float4 *>(o) = a; }
 __device__ __forceinline__ void store4(uint16_t *o, float4 a)
 {
@@ -1283,74 +1281,103 @@ __device__ __forceinline__ void store4(uint16_t *o, float4 a)
     *reinterpret_cast<uint2 *>(o) = w;
 }
 
-// One thread per 4 channels of one grid cell; routes summed in ascending
-// order [OVERVIEW scanning and chunking; SUMMARY 2-D maps].
+// Block shape of the restore/fuse and gather kernels: threadIdx.x walks the
+// 16-byte (or narrower) channel vectors of one token, threadIdx.y the cells,
+// so a token's index math is done once per thread with one 32-bit division
+// at most, and a wave moves whole rows of consecutive tokens.
+struct PlaneShape {
+    int cv = 1, ty = 1;  // vectors per token, tokens per block
+};
+
+PlaneShape plane_shape(int vectors_per_token)
+{
+    PlaneShape s;
+    s.cv = vectors_per_token < 256 ? vectors_per_token : 256;
+    s.ty = 256 / s.cv;
+    return s;
+}
+
+// One thread per 4 channels of one grid cell of batch item b = blockIdx.y
+// (grid-strided); routes summed in ascending order [OVERVIEW scanning and
+// chunking; SUMMARY 2-D maps].
 template <typename OutT>
 __global__ __launch_bounds__(256) void fuse_kernel(const float *__restrict__ y,
                                                    const float *__restrict__ scales,
                                                    OutT *__restrict__ out, int B, int H,
-                                                   int W, int C, unsigned mask,
-                                                   long long nvec)
+                                                   int W, int C, unsigned mask)
 {
-    const long long N = static_cast<long long>(H) * W;
+    const int N = H * W;
     const int C4 = C >> 2;
-    for (long long v = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; v < nvec;
-         v += static_cast<long long>(gridDim.x) * blockDim.x) {
-        const int cv = static_cast<int>(v % C4);
-        const long long pix = v / C4;
-        const long long b = pix / N;
-        const long long cell = pix - b * N;
-        const int i = static_cast<int>(cell / W);
-        const int j = static_cast<int>(cell - static_cast<long long>(i) * W);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int slot = 0;
-        for (int r = 0; r < 4; ++r) {
-            if (!(mask & (1u << r)))
-                continue;
-            const long long t = route_step(r, H, W, N, i, j);
-            const float4 yv = *reinterpret_cast<const float4 *>(
-                y + ((static_cast<long long>(slot) * B + b) * N + t) * C + cv * 4);
-            const float4 s = *reinterpret_cast<const float4 *>(scales + r * C + cv * 4);
-            acc.x = fmaf(s.x, yv.x, acc.x);
-            acc.y = fmaf(s.y, yv.y, acc.y);
-            acc.z = fmaf(s.z, yv.z, acc.z);
-            acc.w = fmaf(s.w, yv.w, acc.w);
-            ++slot;
+    const int pix = blockIdx.x * blockDim.y + threadIdx.y;
+    if (pix >= N)
+        return;
+    const int i = static_cast<int>(static_cast<unsigned>(pix) / static_cast<unsigned>(W));
+    const int j = pix - i * W;
+    int ts[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        ts[r] = static_cast<int>(route_step(r, H, W, N, i, j));
+    for (int b = blockIdx.y; b < B; b += gridDim.y) {
+        for (int cv = threadIdx.x; cv < C4; cv += blockDim.x) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            int slot = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!(mask & (1u << r)))
+                    continue;
+                const float4 yv = *reinterpret_cast<const float4 *>(
+                    y + ((static_cast<long long>(slot) * B + b) * N + ts[r]) * C + cv * 4);
+                const float4 s = *reinterpret_cast<const float4 *>(scales + r * C + cv * 4);
+                acc.x = fmaf(s.x, yv.x, acc.x);
+                acc.y = fmaf(s.y, yv.y, acc.y);
+                acc.z = fmaf(s.z, yv.z, acc.z);
+                acc.w = fmaf(s.w, yv.w, acc.w);
+                ++slot;
+            }
+            store4(out + (static_cast<long long>(b) * N + pix) * C + cv * 4, acc);
         }
-        store4(out + pix * C + cv * 4, acc);
     }
 }
 
 // ------------------------------------------------------------ gather kernel
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> { using type = float4; };
-template <> struct Vec4<uint16_t> { using type = uint2; };
-
-template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(const T *__restrict__ x,
-                                                     T *__restrict__ out, int B, int H,
-                                                     int W, int C, unsigned mask, int R,
-                                                     long long nvec)
+// out[slot][b][t_r(i, j)][:] = x[b][i][j][:] for every active route r, with
+// t_r the step at which route r visits cell (i, j): each token row of x is
+// read once and written to every route slot, moved as V vectors. Cell
+// pix = blockIdx.x * blockDim.y + threadIdx.y in grid order, batch item
+// b = blockIdx.y (grid-strided).
+template <typename V>
+__global__ __launch_bounds__(256) void gather_kernel(const char *__restrict__ x,
+                                                     char *__restrict__ out, int B, int H,
+                                                     int W, int row_bytes, unsigned mask)
 {
-    using V = typename Vec4<T>::type;
-    const long long N = static_cast<long long>(H) * W;
-    const int C4 = C >> 2;
-    for (long long v = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; v < nvec;
-         v += static_cast<long long>(gridDim.x) * blockDim.x) {
-        const int cv = static_cast<int>(v % C4);
-        long long rest = v / C4;
-        const long long t = rest % N;
-        rest /= N;
-        const long long b = rest % B;
-        const int slot = static_cast<int>(rest / B);
-        const int r = nth_route(mask, slot);
-        int i, j;
-        route_cell(r, H, W, N, t, i, j);
-        const V val = *reinterpret_cast<const V *>(
-            x + ((b * H + i) * static_cast<long long>(W) + j) * C + cv * 4);
-        *reinterpret_cast<V *>(out + ((static_cast<long long>(slot) * B + b) * N + t) * C +
-                               cv * 4) = val;
+    const int N = H * W;
+    const int pix = blockIdx.x * blockDim.y + threadIdx.y;
+    if (pix >= N)
+        return;
+    const int i = static_cast<int>(static_cast<unsigned>(pix) / static_cast<unsigned>(W));
+    const int j = pix - i * W;
+    int ts[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        ts[r] = static_cast<int>(route_step(r, H, W, N, i, j));
+    const int nv = row_bytes / static_cast<int>(sizeof(V));
+    for (int b = blockIdx.y; b < B; b += gridDim.y) {
+        const V *src = reinterpret_cast<const V *>(
+            x + (static_cast<long long>(b) * N + pix) * row_bytes);
+        for (int cv = threadIdx.x; cv < nv; cv += blockDim.x) {
+            const V val = src[cv];
+            int slot = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!(mask & (1u << r)))
+                    continue;
+                V *dst = reinterpret_cast<V *>(
+                    out + ((static_cast<long long>(slot) * B + b) * N + ts[r]) * row_bytes);
+                dst[cv] = val;
+                ++slot;
+            }
+        }
     }
 }
 
@@ -1749,15 +1776,15 @@ srnl_status srnl_fuse(const float *y, int B, int H, int W, int C, unsigned route
         return SRNL_OK;
     if (!is_device_ptr(y) || !is_device_ptr(scales) || !is_device_ptr(out))
         return fail(SRNL_ERR_PTR, "y_routes, scales and out must be device memory");
-    const long long nvec = static_cast<long long>(B) * H * W * (C / 4);
-    const int grid = grid_for(nvec, 256);
+    const PlaneShape ps = plane_shape(C / 4);
+    const dim3 grid((H * W + ps.ty - 1) / ps.ty, B < 65535 ? B : 65535), block(ps.cv, ps.ty);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (out_dtype == SRNL_F32)
-        hipLaunchKernelGGL(fuse_kernel<float>, dim3(grid), dim3(256), 0, st, y, scales,
-                           static_cast<float *>(out), B, H, W, C, route_mask, nvec);
+        hipLaunchKernelGGL(fuse_kernel<float>, grid, block, 0, st, y, scales,
+                           static_cast<float *>(out), B, H, W, C, route_mask);
     else
-        hipLaunchKernelGGL(fuse_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, y, scales,
-                           static_cast<uint16_t *>(out), B, H, W, C, route_mask, nvec);
+        hipLaunchKernelGGL(fuse_kernel<uint16_t>, grid, block, 0, st, y, scales,
+                           static_cast<uint16_t *>(out), B, H, W, C, route_mask);
     return launch_check("fuse_kernel");
 }
 
@@ -1854,18 +1881,27 @@ srnl_status srnl_route_gather(const void *x, int B, int H, int W, int C, unsigne
         return SRNL_OK;
     if (!is_device_ptr(x) || !is_device_ptr(out))
         return fail(SRNL_ERR_PTR, "x and out must be device memory");
-    const int R = popcount4(route_mask);
-    const long long nvec = n / 4;
-    const int grid = grid_for(nvec, 256);
+    const int row_bytes = C * (dtype == SRNL_F32 ? 4 : 2);
+    const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(out) |
+                            static_cast<uintptr_t>(row_bytes);
+    const int vb = (align % 16 == 0) ? 16 : (align % 8 == 0) ? 8 : (align % 4 == 0) ? 4 : 2;
+    const PlaneShape ps = plane_shape(row_bytes / vb);
+    const dim3 grid((H * W + ps.ty - 1) / ps.ty, B < 65535 ? B : 65535), block(ps.cv, ps.ty);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dtype == SRNL_F32)
-        hipLaunchKernelGGL(gather_kernel<float>, dim3(grid), dim3(256), 0, st,
-                           static_cast<const float *>(x), static_cast<float *>(out), B, H, W,
-                           C, route_mask, R, nvec);
+    const char *xs = static_cast<const char *>(x);
+    char *os = static_cast<char *>(out);
+    if (vb == 16)
+        hipLaunchKernelGGL(gather_kernel<uint4>, grid, block, 0, st, xs, os, B, H, W, row_bytes,
+                           route_mask);
+    else if (vb == 8)
+        hipLaunchKernelGGL(gather_kernel<uint2>, grid, block, 0, st, xs, os, B, H, W, row_bytes,
+                           route_mask);
+    else if (vb == 4)
+        hipLaunchKernelGGL(gather_kernel<uint32_t>, grid, block, 0, st, xs, os, B, H, W,
+                           row_bytes, route_mask);
     else
-        hipLaunchKernelGGL(gather_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(x), static_cast<uint16_t *>(out), B,
-                           H, W, C, route_mask, R, nvec);
+        hipLaunchKernelGGL(gather_kernel<uint16_t>, grid, block, 0, st, xs, os, B, H, W,
+                           row_bytes, route_mask);
     return launch_check("gather_kernel");
 }
 

@@ -154,6 +154,35 @@ def test_route_gather_bit_exact(dtype, B, H, W, C, mask):
         assert torch.equal(g[s], xf[:, idx])
 
 
+@pytest.mark.parametrize("dtype,offset", [(torch.bfloat16, 1), (torch.bfloat16, 2),
+                                          (torch.bfloat16, 4), (torch.float32, 1),
+                                          (torch.float32, 2)])
+@pytest.mark.parametrize("C", [4, 12, 2052])
+def test_route_gather_unaligned_views_and_wide_rows(dtype, offset, C):
+    """Views that start 2, 4 or 8 bytes past an aligned address take the
+    narrower copy widths; rows wider than 256 vectors loop over channels."""
+    B, H, W, mask = 2, 3, 5, 15
+    base = _dev(synth.normals(8, 1, B * H * W * C + offset), dtype)
+    x = base[offset:].view(B, H, W, C)
+    g = srnl.route_gather(x, mask)
+    xf = x.reshape(B, H * W, C)
+    for r in range(4):
+        cells = [oracle.route_index(r, H, W, t) for t in range(H * W)]
+        idx = torch.tensor([i * W + j for i, j in cells], device=DEV)
+        assert torch.equal(g[r], xf[:, idx])
+
+
+def test_fuse_wide_rows():
+    """C = 1028: more 4-channel vectors per token (257) than a block holds."""
+    B, H, W, C, mask = 2, 3, 2, 1028, 15
+    y = synth.normals(4, 1, 4 * B * H * W * C).reshape(4, B, H * W, C).astype(np.float32)
+    sc = synth.scales(4, C)
+    out = srnl.fuse(_dev(y, torch.float32), B, H, W, C, mask,
+                    _dev(sc, torch.float32)).double().cpu().numpy()
+    exp = oracle.fuse(y.astype(np.float64), B, H, W, C, mask, sc)
+    assert np.abs(out - exp).max() <= 1e-6 * np.abs(exp).max()
+
+
 @pytest.mark.parametrize("mask", [1, 2, 4, 8, 6, 15])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_fuse_matches_oracle(mask, out_dtype):
