@@ -509,7 +509,7 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int NTC = D / 16;             // 16-wide column tiles of d
     static constexpr int NWIN = T / 16;            // windows per sub-block
     static constexpr int ETS = T + 4;              // [channel][token] row stride
-    static constexpr int WS = 20;                  // row stride of the per-window N tables
+    static constexpr int WS = 20;                  // row stride of the per-window N and L tables
     static constexpr int JS = (NW >= 2 * NTC) ? 2 : 1;   // waves sharing 16 rows of Q
     static constexpr int NJ = NTC / JS;            // 16-column tiles of Q per wave
     static constexpr int CW = NTC * JS;            // waves in the token-order update
@@ -523,7 +523,7 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     // the windows' L tables; the v rows (dead after the epilogue) hold the
     // N and T' tables, and at a chunk end Q_L^T when it fits.
     static constexpr int SZ_TOK = T * LDP;
-    static constexpr int SZ_LC = NWIN * 256;
+    static constexpr int SZ_LC = NWIN * 16 * WS;
     static constexpr int SZ_NN = NWIN * 16 * WS;
     static constexpr int SZ_TP = NWIN * 256;
     static constexpr int SZ_QT = D * LDP;
@@ -691,6 +691,13 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const QVa = pool + Cfg::O_QV;   // separate query rows q_t (HAS_Q)
     float *const Qt = pool + Cfg::O_QT;    // Q_L^T at a chunk end
     const float *const QR = HAS_Q ? QVa : Xs;   // query rows
+    // Token column of e in its [channel][token] layout, XOR-swizzled by the
+    // channel's group of 8: the epilogue's lanes each store 8 consecutive
+    // channels of one token, and unswizzled the groups of a half-wave would
+    // share LDS banks. Aligned groups of 4 tokens stay contiguous.
+    constexpr int EPL0 = NT / T;
+    static_assert(D / EPL0 == 8 && 32 % EPL0 == 0 && T % 32 == 0, "e layout swizzle");
+    auto et_col = [](int row, int u) { return u ^ (((row >> 3) & (EPL0 - 1)) * (32 / EPL0)); };
 
     const int chain = xcd_remap(blockIdx.x, gridDim.x);
     if (chain >= nchains)
@@ -899,7 +906,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                         khv[4 * c4 + 3]);
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c)
-                    Et[(c0e + c) * ETS + u] = evv[c];
+                    Et[(c0e + c) * ETS + et_col(c0e + c, u)] = evv[c];
                 nkh2 = group_sum<EPL>(nkh2);
                 ne2 = group_sum<EPL>(ne2);
                 const float eta = sigmoidf(er);
@@ -935,7 +942,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     st4(KHa + u * LDP + c0e + 4 * c4, 0.f, 0.f, 0.f, 0.f);
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c)
-                    Et[(c0e + c) * ETS + u] = 0.f;
+                    Et[(c0e + c) * ETS + et_col(c0e + c, u)] = 0.f;
                 if (ep == 0) {
                     AL[u] = 1.0f;
                     EH[u] = 0.0f;
@@ -1003,7 +1010,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     Rr[i] = P[i] * at;
             }
             float Nr[4], Lr[4];
-            float *lc = Lc + win * 256;
+            float *lc = Lc + win * 16 * WS;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 4 * lk + i;
@@ -1012,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 Lr[i] = lt ? et * P[i] * gkk[i] : 0.0f;
                 Nr[i] = BEFORE ? (lt ? P[i] * gqk[i] : 0.0f) : Rr[i] * gqk[i];
             }
-            st4(lc + t * 16 + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
+            st4(lc + t * WS + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
             st4(Nn + win * 16 * WS + t * WS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
             if (t == 15)
                 st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
@@ -1034,7 +1041,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 float lrow[4][16];   // L[4 g + i][m]
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    lds_load(lc + (4 * g + i) * 16, lrow[i]);
+                    lds_load(lc + (4 * g + i) * WS, lrow[i]);
                 float acc[4], xf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1110,7 +1117,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 const float4 ga = ld4(GA + tb + 4 * lk);
                 const float4 gz = ld4(GZ + tb + 4 * lk);
                 const float4 rb = ld4(RB + tb + 4 * lk);
-                const float4 ee = ld4(Et + (16 * it + lm) * ETS + tb + 4 * lk);
+                const float4 ee = ld4(Et + (16 * it + lm) * ETS + et_col(16 * it + lm, tb + 4 * lk));
                 const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
                 const float4 nnv = ld4(Nn + win * 16 * WS + lm * WS + 4 * lk);
                 const float wg = WG[win];
