@@ -268,6 +268,70 @@ def main_seq1d(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_stages(args):
+    """Forward (scan + fuse, four routes) on every stage shape: the four
+    hierarchical stages at batch 64 (56x56/C=64/2 heads, 28x28/C=128/4,
+    14x14/C=256/8, 7x7/C=512/16, d=32, N(0,1), seed 3), the plain-backbone
+    map (batch 32, 14x14, C=192, 3 heads x d=64, seed 1) and the
+    dense-prediction map (batch 2, 200x304, C=64, 2 heads x d=32, 5 % of the
+    tokens x50, seed 4); bf16 input, fp32 state. value = tokens*heads/s of
+    one pass over the four hierarchical stages."""
+    import torch
+    from self_referential_memory_amd import srnl, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wls = synth.hier_sweep() + [synth.plain14(), synth.dense200x304()]
+    stages = []
+    for wl in wls:
+        x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+        st = torch.from_numpy(wl.states).to(dev)
+        sc = torch.from_numpy(wl.scales).to(dev)
+        y = torch.empty((4, wl.B, wl.N, wl.C), dtype=torch.float32, device=dev)
+        out = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.bfloat16, device=dev)
+        p = srnl.make_params(st, x, alpha_max=wl.alpha_max, eps=wl.eps,
+                             chunk_row=wl.chunk_row, chunk_col=wl.chunk_col)
+        steps = args.steps
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+               for _ in range(steps)]
+        for i in range(args.warmup + steps):
+            e = evs[i - args.warmup] if i >= args.warmup else None
+            if e is not None:
+                e[0].record()
+            srnl.scan_fwd(x, st, wl.heads, wl.d, 15, out=y, params=p)
+            if e is not None:
+                e[1].record()
+            srnl.fuse(y, wl.B, wl.H, wl.W, wl.C, 15, sc, out=out)
+            if e is not None:
+                e[2].record()
+        torch.cuda.synchronize()
+        scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        step_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+        units = wl.B * wl.N * wl.heads
+        flops = algorithmic_flops_per_unit(wl.d) * units * 4
+        stages.append({"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C,
+                       "heads": wl.heads, "d": wl.d, "chains": 4 * wl.B * wl.heads,
+                       "chunk": [wl.chunk_row or wl.W, wl.chunk_col or wl.H],
+                       "ms_per_step": step_ms, "scan_ms": scan_ms,
+                       "tokens_heads_per_s": units / (step_ms / 1000.0),
+                       "mfma_frac": flops / (scan_ms / 1000.0) / 1e12 / PEAK_FP32_MFMA_TFLOPS})
+        print(f"[stage] {wl.name}: {step_ms:.3f} ms/step, scan {scan_ms:.3f} ms", file=sys.stderr,
+              flush=True)
+        del x, y, out
+    hier = stages[:4]
+    tot_units = sum(s["B"] * s["H"] * s["W"] * s["heads"] for s in hier)
+    tot_ms = sum(s["ms_per_step"] for s in hier)
+    rec = {"metric": "SRNL fwd tokens·heads/s (4 routes), one pass over the hierarchical stages",
+           "value": tot_units / (tot_ms / 1000.0), "unit": "tokens·heads/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": tot_ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "stages: hierarchical sweep 56/28/14/7 at batch 64, plus "
+                                  "plain14 and dense200x304 (reported per stage)",
+                      "parallelism": "single GPU"},
+           "stages": stages}
+    print(json.dumps(rec), flush=True)
+
+
 def main_hier56_bwd(args):
     """Backward of the hier56 step: srnl_fuse_bwd + srnl_scan_bwd for a given
     dL/d(fused output), forward outputs and inputs resident in HBM."""
@@ -361,9 +425,11 @@ def main():
     ap.add_argument("--pmc-passes", action="store_true",
                     help="print the counter passes, one line each: NAME COUNTER...")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
-    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd"), default="hier56",
+    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "stages"),
+                    default="hier56",
                     help="hier56: the 2-D four-route operator (default); seq1d: the "
-                         "standalone 1-D SRNL; hier56_bwd: its backward pass")
+                         "standalone 1-D SRNL; hier56_bwd: its backward pass; stages: the "
+                         "forward on every stage shape")
     args = ap.parse_args()
     if args.pmc_passes:
         for name, counters in PMC_PASSES:
@@ -382,6 +448,9 @@ def main():
         return
     if args.workload == "hier56_bwd":
         main_hier56_bwd(args)
+        return
+    if args.workload == "stages":
+        main_stages(args)
         return
 
     import numpy as np

@@ -508,12 +508,16 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int KS = D / 4;               // MFMA K-steps over d
     static constexpr int NTC = D / 16;             // 16-wide column tiles of d
     static constexpr int NWIN = T / 16;            // windows per sub-block
-    static constexpr int ETS = T + 4;              // [channel][token] row stride
+    static constexpr int EPL = NT / T;             // epilogue lanes per token
+    static constexpr int ECPL = D / EPL;           // channels per epilogue lane
+    static constexpr int TE = T > 32 ? T : 32;     // token columns of the e rows
+    static constexpr int ETS = TE + 4;             // [channel][token] row stride
     static constexpr int WS = 20;                  // row stride of the per-window N and L tables
     static constexpr int JS = (NW >= 2 * NTC) ? 2 : 1;   // waves sharing 16 rows of Q
     static constexpr int NJ = NTC / JS;            // 16-column tiles of Q per wave
     static constexpr int CW = NTC * JS;            // waves in the token-order update
     static_assert(T % 16 == 0 && T <= 64, "sub-block of whole windows");
+    static_assert(EPL * T == NT && EPL >= 2 && EPL <= 16 && ECPL % 4 == 0, "epilogue lanes");
     static_assert(NW >= NTC, "one wave per 16 rows of Q");
     static_assert(NTC % JS == 0 && (JS == 1 || CW == NW), "column split over whole tiles, all waves");
     static_assert(NT >= 2 * D, "vector-memory refresh: one thread per output");
@@ -529,6 +533,9 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int SZ_QT = D * LDP;
     static_assert(SZ_LC <= SZ_TOK && SZ_NN + SZ_TP <= SZ_TOK, "window tables fit");
     static constexpr bool QT_IN_ES = SZ_QT <= SZ_TOK;
+    // else, when it fits, over the x, k/z, v and k^ rows (contiguous), which
+    // are dead at a chunk end once the readout has read the z rows
+    static constexpr bool QT_IN_TOK = !QT_IN_ES && SZ_QT <= 4 * SZ_TOK;
     static constexpr int O_BS = 0;
     static constexpr int O_XS = O_BS + ROWS * LDP;
     static constexpr int O_KZ = O_XS + SZ_TOK;
@@ -546,8 +553,9 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int SZ_XB = (JS == 2) ? 2 * NTC * 512 : 0;
     static constexpr int O_KZ2 = O_XB + SZ_XB;
     static constexpr int O_QV = O_KZ2 + ((JS == 2) ? SZ_TOK : 0);
-    static constexpr int O_QT = QT_IN_ES ? O_ES : O_QV + (HAS_Q ? SZ_TOK : 0);
-    static constexpr int POOL = (QT_IN_ES ? O_QV : O_QT + SZ_QT) + (HAS_Q ? SZ_TOK : 0);
+    static constexpr int O_QT = QT_IN_ES ? O_ES : QT_IN_TOK ? O_XS : O_QV + (HAS_Q ? SZ_TOK : 0);
+    static constexpr int POOL =
+        ((QT_IN_ES || QT_IN_TOK) ? O_QV : O_QT + SZ_QT) + (HAS_Q ? SZ_TOK : 0);
 };
 
 // Index of T'[s][t] in a window's 16 x 16 table: rows of 16 floats, the four
@@ -586,6 +594,8 @@ template <int G> __device__ __forceinline__ float group_sum(float v)
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)); // xor 2
     if (G >= 8)   // row_half_mirror: lane i <- lane 7-i within each group of 8
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+    if (G >= 16)  // row_mirror: lane i <- lane 15-i within each row of 16
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
     return v;
 }
 
@@ -692,12 +702,15 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const Qt = pool + Cfg::O_QT;    // Q_L^T at a chunk end
     const float *const QR = HAS_Q ? QVa : Xs;   // query rows
     // Token column of e in its [channel][token] layout, XOR-swizzled by the
-    // channel's group of 8: the epilogue's lanes each store 8 consecutive
-    // channels of one token, and unswizzled the groups of a half-wave would
-    // share LDS banks. Aligned groups of 4 tokens stay contiguous.
-    constexpr int EPL0 = NT / T;
-    static_assert(D / EPL0 == 8 && 32 % EPL0 == 0 && T % 32 == 0, "e layout swizzle");
-    auto et_col = [](int row, int u) { return u ^ (((row >> 3) & (EPL0 - 1)) * (32 / EPL0)); };
+    // epilogue lane that stores the channel: those lanes each store ECPL
+    // consecutive channels of one token, and unswizzled the lanes of a
+    // half-wave would share LDS banks. The XOR is a multiple of 4 below TE,
+    // so aligned groups of 4 tokens stay contiguous and in the row.
+    constexpr int EPL = Cfg::EPL, ECPL = Cfg::ECPL, TE = Cfg::TE;
+    constexpr int ET_SW = (32 / EPL < 4) ? 4 : 32 / EPL;
+    auto et_col = [](int row, int u) {
+        return u ^ ((((row / ECPL) & (EPL - 1)) * ET_SW) & (TE - 4));
+    };
 
     const int chain = xcd_remap(blockIdx.x, gridDim.x);
     if (chain >= nchains)
@@ -868,9 +881,6 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     k^ = k / sqrt(|k|^2 + eps), e = k^ - v, eta = sigmoid(b_eta . x),
         //     alpha = alpha_max sigmoid(b_alpha . x), soft cap, spectral clamp.
         {
-            constexpr int EPL = NT / T;
-            constexpr int ECPL = D / EPL;
-            static_assert(EPL * T == NT && (EPL == 2 || EPL == 4 || EPL == 8), "epilogue lanes");
             const int u = tid / EPL, ep = tid % EPL;
             const int c0e = ep * ECPL;
             if (u < nt) {
@@ -1217,6 +1227,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         if (chunk_end) {
             if (cend < N) {
                 // (7) refresh the boundary: B <- B Q_L (tiles split over the waves)
+                if constexpr (Cfg::QT_IN_TOK)
+                    __syncthreads();   // the readout is done with the z rows under Q_L^T
                 if (wave < CW) {
                     const int it = wave % NTC, jg = wave / NTC;
 #pragma unroll
@@ -1490,9 +1502,49 @@ int grid_for(long long work, int block)
     return static_cast<int>(g < 1 ? 1 : g);
 }
 
-// waves per chain and tokens per sub-block of the MFMA scan kernel
-template <int D> struct MfmaNW { static constexpr int value = 4; };
-template <int D> struct MfmaT { static constexpr int value = (D == 32) ? 64 : 32; };
+// Sub-block length T (tokens) of the MFMA scan kernel, from the longest
+// chunk of the active routes: a chunk no longer than 16 or 32 tokens takes a
+// sub-block of that length, whose smaller LDS footprint fits more chains on a
+// CU. Waves per chain NW: 2 for d = 32 at T = 16, else 4.
+template <int D> struct MfmaTMax { static constexpr int value = (D == 32) ? 64 : 32; };
+template <int D, int T> struct MfmaNW { static constexpr int value = (D == 32 && T == 16) ? 2 : 4; };
+
+int longest_chunk(int H, int W, unsigned mask, int chunk_row, int chunk_col)
+{
+    const long long N = static_cast<long long>(H) * W;
+    long long L = 0;
+    for (int r = 0; r < 4; ++r) {
+        if (!(mask & (1u << r)))
+            continue;
+        long long l = (r < 2) ? (chunk_row > 0 ? chunk_row : W) : (chunk_col > 0 ? chunk_col : H);
+        if (l > N)
+            l = N;
+        if (l > L)
+            L = l;
+    }
+    return static_cast<int>(L);
+}
+
+template <int D, int T, typename InT>
+void launch_scan_mfma(const void *x, const srnl_params *p, int B, int H, int W, int C,
+                      int heads, unsigned mask, int R, int nchains, int nblocks, float *out)
+{
+    constexpr int NW = MfmaNW<D, T>::value;
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    const bool before = (p->flags & F_READ_BEFORE) != 0, has_q = p->q != nullptr;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(nblocks), dim3(NW * 64), 0, st,
+                           static_cast<const InT *>(x), static_cast<const InT *>(p->q),
+                           p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                           p->chunk_row, p->chunk_col, p->flags, nchains);
+    };
+    if (before)
+        has_q ? go(scan_mfma_kernel<D, NW, T, true, true, InT>)
+              : go(scan_mfma_kernel<D, NW, T, true, false, InT>);
+    else
+        has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT>)
+              : go(scan_mfma_kernel<D, NW, T, false, false, InT>);
+}
 
 template <int D, typename InT>
 srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W, int C,
@@ -1503,29 +1555,23 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
     if (nchains > INT_MAX - 8)
         return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
     const int nblocks = static_cast<int>((nchains + 7) / 8 * 8);
-    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    const int nc = static_cast<int>(nchains);
     if constexpr (D >= 32) {
-        constexpr int T = MfmaT<D>::value;
-        constexpr int NW = MfmaNW<D>::value;
-        const bool before = (p->flags & F_READ_BEFORE) != 0, has_q = p->q != nullptr;
-        auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3(nblocks), dim3(NW * 64), 0, st,
-                               static_cast<const InT *>(x), static_cast<const InT *>(p->q),
-                               p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
-                               p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
-        };
-        if (before)
-            has_q ? go(scan_mfma_kernel<D, NW, T, true, true, InT>)
-                  : go(scan_mfma_kernel<D, NW, T, true, false, InT>);
+        const int L = longest_chunk(H, W, mask, p->chunk_row, p->chunk_col);
+        if (L <= 16)
+            launch_scan_mfma<D, 16, InT>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out);
+        else if (L <= 32 || MfmaTMax<D>::value == 32)
+            launch_scan_mfma<D, 32, InT>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out);
         else
-            has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT>)
-                  : go(scan_mfma_kernel<D, NW, T, false, false, InT>);
+            launch_scan_mfma<D, MfmaTMax<D>::value, InT>(x, p, B, H, W, C, heads, mask, R, nc,
+                                                         nblocks, out);
         return launch_check("scan_mfma_kernel");
     } else {
+        hipStream_t st = static_cast<hipStream_t>(p->stream);
         hipLaunchKernelGGL((scan_simple_kernel<D, InT>), dim3(nblocks), dim3(ScanCfg<D>::NT), 0,
                            st, static_cast<const InT *>(x), static_cast<const InT *>(p->q),
                            p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
-                           p->chunk_row, p->chunk_col, p->flags, static_cast<int>(nchains));
+                           p->chunk_row, p->chunk_col, p->flags, nc);
         return launch_check("scan_simple_kernel");
     }
 }
