@@ -1505,9 +1505,9 @@ int grid_for(long long work, int block)
 // Sub-block length T (tokens) of the MFMA scan kernel, from the longest
 // chunk of the active routes: a chunk no longer than 16 or 32 tokens takes a
 // sub-block of that length, whose smaller LDS footprint fits more chains on a
-// CU. Waves per chain NW: 2 for d = 32 at T = 16, else 4.
+// CU. Waves per chain NW: 2 for d = 32 at T <= 32, else 4.
 template <int D> struct MfmaTMax { static constexpr int value = (D == 32) ? 64 : 32; };
-template <int D, int T> struct MfmaNW { static constexpr int value = (D == 32 && T == 16) ? 2 : 4; };
+template <int D, int T> struct MfmaNW { static constexpr int value = (D == 32 && T <= 32) ? 2 : 4; };
 
 int longest_chunk(int H, int W, unsigned mask, int chunk_row, int chunk_col)
 {
