@@ -516,10 +516,10 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int JS = (NW >= 2 * NTC) ? 2 : 1;   // waves sharing 16 rows of Q
     static constexpr int NJ = NTC / JS;            // 16-column tiles of Q per wave
     static constexpr int CW = NTC * JS;            // waves in the token-order update
-    static_assert(T % 16 == 0 && T <= 64, "sub-block of whole windows");
+    static_assert(T % 16 == 0 && T <= 128, "sub-block of whole windows");
     static_assert(EPL * T == NT && EPL >= 2 && EPL <= 16 && ECPL % 4 == 0, "epilogue lanes");
     static_assert(NW >= NTC, "one wave per 16 rows of Q");
-    static_assert(NTC % JS == 0 && (JS == 1 || CW == NW), "column split over whole tiles, all waves");
+    static_assert(NTC % JS == 0 && CW <= NW, "column split over whole tiles");
     static_assert(NT >= 2 * D, "vector-memory refresh: one thread per output");
 
     // LDS pool (floats). Arrays that are dead in a phase lend their space:
@@ -676,8 +676,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
     constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
     constexpr int RT = (3 * D / 16) * NTC;             // refresh tiles (matrix memories)
-    static_assert(RT % NW == 0, "refresh tiles split evenly over waves");
-    constexpr int RTW = RT / NW;                       // refresh tiles per wave
+    constexpr int RTW = (RT + NW - 1) / NW;            // refresh tiles per wave (at most)
 
     __shared__ __align__(16) float pool[Cfg::POOL];
     float *const Bs = pool + Cfg::O_BS;    // boundary rows M_c, M_k, M_v, m_eta, m_alpha
@@ -764,6 +763,19 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 qacc[jl][i] = (16 * (jg * NJ + jl) + 4 * lk + i == 16 * it + lm) ? 1.0f : 0.0f;
     };
     reset_q();
+    // Q_L^T into LDS for the boundary refresh (waves < CW)
+    auto stage_qt = [&]() {
+        const int it = wave % NTC, jg = wave / NTC;
+#pragma unroll
+        for (int jl = 0; jl < NJ; ++jl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                Qt[(16 * (jg * NJ + jl) + 4 * lk + i) * LDP + 16 * it + lm] = qacc[jl][i];
+    };
+    // With two waves per 16 rows of Q, every window ends in a block barrier
+    // after the window's table reads, so Q_L^T can be staged at the end of the
+    // update, over the tables, when it does not cover rows the readout reads.
+    constexpr bool QT_EARLY = JS == 2 && !Cfg::QT_IN_TOK;
 
     const size_t out_row0 = (static_cast<size_t>(slot) * B + b) * N;
 
@@ -1185,8 +1197,23 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 for (int i = 0; i < 4; ++i)
                     zd[(tb + 4 * lk + i) * LDP + 16 * it + lm] = Z[i];
             }
+            if constexpr (QT_EARLY) {
+                if (chunk_end && cend < N)
+                    stage_qt();
+            }
+        } else if constexpr (JS == 2) {
+            // the update's per-window block barrier, for the waves outside it
+            for (int win = 0; win < nwin; ++win)
+                __syncthreads();
         }
         __syncthreads();
+        if constexpr (!QT_EARLY && !Cfg::QT_IN_TOK) {
+            if (chunk_end && cend < N) {
+                if (wave < CW)
+                    stage_qt();
+                __syncthreads();
+            }
+        }
 
         // (6) readout on MFMA: Y^T = B_c Z^T, so that each lane holds four
         //     consecutive channels of one token (16-byte stores). With more
@@ -1226,22 +1253,21 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 
         if (chunk_end) {
             if (cend < N) {
-                // (7) refresh the boundary: B <- B Q_L (tiles split over the waves)
-                if constexpr (Cfg::QT_IN_TOK)
-                    __syncthreads();   // the readout is done with the z rows under Q_L^T
-                if (wave < CW) {
-                    const int it = wave % NTC, jg = wave / NTC;
-#pragma unroll
-                    for (int jl = 0; jl < NJ; ++jl)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            Qt[(16 * (jg * NJ + jl) + 4 * lk + i) * LDP + 16 * it + lm] = qacc[jl][i];
+                // (7) refresh the boundary: B <- B Q_L (tiles split over the
+                //     waves). Q_L^T is staged already unless it covers the z
+                //     rows, which the readout above had to finish with first.
+                if constexpr (Cfg::QT_IN_TOK) {
+                    __syncthreads();
+                    if (wave < CW)
+                        stage_qt();
+                    __syncthreads();
                 }
-                __syncthreads();
                 v4f racc[RTW];
 #pragma unroll
                 for (int w = 0; w < RTW; ++w) {
                     const int tile = wave + w * NW;
+                    if (RT % NW != 0 && tile >= RT)
+                        break;
                     const int tm = tile / NTC, tn = tile % NTC;
                     float a[KS], bq[KS];
                     lds_load(Bs + (tm * 16 + lm) * LDP + lk * KS, a);
@@ -1270,6 +1296,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int w = 0; w < RTW; ++w) {
                     const int tile = wave + w * NW;
+                    if (RT % NW != 0 && tile >= RT)
+                        break;
                     const int tm = tile / NTC, tn = tile % NTC;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
@@ -1505,9 +1533,15 @@ int grid_for(long long work, int block)
 // Sub-block length T (tokens) of the MFMA scan kernel, from the longest
 // chunk of the active routes: a chunk no longer than 16 or 32 tokens takes a
 // sub-block of that length, whose smaller LDS footprint fits more chains on a
-// CU. Waves per chain NW: 2 for d = 32 at T <= 32, else 4.
+// CU. Longer chunks take 64 tokens at d = 32 (32 at d = 64); at d = 32, when
+// there are no more chains than CUs, 128 tokens on 8 waves, which halves the
+// per-token latency of every phase but the token-order update. Waves per
+// chain NW: 2 for d = 32 at T <= 32, 8 at T = 128, else 4.
 template <int D> struct MfmaTMax { static constexpr int value = (D == 32) ? 64 : 32; };
-template <int D, int T> struct MfmaNW { static constexpr int value = (D == 32 && T <= 32) ? 2 : 4; };
+template <int D, int T> struct MfmaNW {
+    static constexpr int value = (D == 32 && T <= 32) ? 2 : (T == 128) ? 8 : 4;
+};
+constexpr int kFewChains = 256;   // one chain per CU at most
 
 int longest_chunk(int H, int W, unsigned mask, int chunk_row, int chunk_col)
 {
@@ -1562,6 +1596,9 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
             launch_scan_mfma<D, 16, InT>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out);
         else if (L <= 32 || MfmaTMax<D>::value == 32)
             launch_scan_mfma<D, 32, InT>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out);
+        else if (D == 32 && L > 64 && nc <= kFewChains)
+            launch_scan_mfma<D, (D == 32 ? 128 : 32), InT>(x, p, B, H, W, C, heads, mask, R, nc,
+                                                           nblocks, out);
         else
             launch_scan_mfma<D, MfmaTMax<D>::value, InT>(x, p, B, H, W, C, heads, mask, R, nc,
                                                          nblocks, out);

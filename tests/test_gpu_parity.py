@@ -295,20 +295,24 @@ def test_clamp_binds_in_adversarial_parity_case():
     assert (tr[..., 13] < tr[..., 12]).mean() > 0.001
 
 
-# The scan kernel takes a 16-, 32- or 64-token sub-block from the longest
-# chunk (d = 32: <= 16, <= 32, longer; d = 64: <= 16, longer). Each of those
-# configurations, on large states (std 2) with x50 outlier tokens, where the
-# clamp binds on 1-3 % of the tokens, with variant flags, both input dtypes
-# and separate queries. At std 2 no chunk of these grids moves by more than
-# 2.2e-4 of its scale when the inputs are perturbed at the fp32 rounding
-# level in exact arithmetic; at std 3 one chunk of the 14x14 d = 64 grid
-# moves by 1.3e-3, beyond the per-chunk bar for any fp32 evaluation.
+# The scan kernel picks its sub-block from the longest chunk: at d = 32, 16
+# or 32 tokens (on two waves) for chunks that fit, else 64 tokens, or 128 on
+# eight waves when there are at most 256 chains; at d = 64, 16 or 32 tokens.
+# Each configuration runs on large states with x50 outlier tokens, where the
+# clamp binds on 1-5 % of the tokens, with variant flags, both input dtypes
+# and separate queries. The states are chosen so that no chunk of a grid
+# moves by more than 2.2e-4 of its scale when the inputs are perturbed at the
+# fp32 rounding level in exact arithmetic (std 3 puts a chunk of the 14x14
+# d = 64 grid at 1.3e-3, beyond the per-chunk bar for any fp32 evaluation).
 SUB_BLOCK_GRIDS = [
-    ("sb16_d32", 2, 12, 10, 32, 2, 0, 0),
-    ("sb32_d32", 2, 20, 28, 32, 2, 0, 0),
-    ("sb64_d32", 1, 10, 55, 32, 2, 45, 0),     # 45-token row chunks, ragged last chunk
-    ("sb16_d64", 2, 14, 14, 64, 1, 0, 0),
-    ("sb32_d64", 1, 24, 20, 64, 1, 0, 0),
+    # name, B, H, W, d, heads, chunk_row, chunk_col, state_std, outlier_frac
+    ("sb16_d32", 2, 12, 10, 32, 2, 0, 0, 2.0, 0.05),
+    ("sb32_d32", 2, 20, 28, 32, 2, 0, 0, 2.0, 0.05),
+    ("sb64_d32", 1, 10, 55, 32, 2, 45, 0, 2.0, 0.05),    # 45-token row chunks, ragged tail
+    ("sb128_d32", 1, 6, 150, 32, 2, 0, 0, 2.0, 0.05),   # 8 chains; 150 = 128 + 22
+    ("sb64x2_d32", 40, 3, 100, 32, 2, 0, 0, 0.5, 0.0),  # 320 chains; 100 = 64 + 36
+    ("sb16_d64", 2, 14, 14, 64, 1, 0, 0, 2.0, 0.05),
+    ("sb32_d64", 1, 24, 20, 64, 1, 0, 0, 2.0, 0.05),
 ]
 SUB_BLOCK_VARIANTS = [
     (0, "bf16", False),
@@ -322,10 +326,10 @@ SUB_BLOCK_VARIANTS = [
 @pytest.mark.parametrize("variant", SUB_BLOCK_VARIANTS, ids=["plain", "before_q", "hardcap_noclamp",
                                                               "fixedalpha_q"])
 def test_sub_block_configurations(grid, variant):
-    name, B, H, W, d, heads, cr, cc = grid
+    name, B, H, W, d, heads, cr, cc, std, outl = grid
     flags, dtype, q = variant
-    wl = synth.make(name, B, H, W, heads * d, heads, d, dtype, 21, state_std=2.0,
-                    outlier_frac=0.05, separate_q=q, chunk_row=cr, chunk_col=cc)
+    wl = synth.make(name, B, H, W, heads * d, heads, d, dtype, 21, state_std=std,
+                    outlier_frac=outl, separate_q=q, chunk_row=cr, chunk_col=cc)
     check(wl, flags=flags)
 
 
