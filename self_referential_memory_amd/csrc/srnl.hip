@@ -504,7 +504,12 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int NW = NW_;                 // waves per chain
     static constexpr int NT = NW * 64;             // threads
     static constexpr int ROWS = 3 * D + 2;
-    static constexpr int LDP = D + 4;              // [token][channel] row stride
+    // [row][channel] arrays: at d = 32 with sub-blocks of 64 or 128 tokens,
+    // unpadded rows whose 16-byte blocks are XOR-swizzled by the row
+    // (swz_row); else rows padded by 4 floats (for the two-wave sub-blocks
+    // the swizzle's address arithmetic costs more than the conflicts it saves)
+    static constexpr bool SWZ = D == 32 && T >= 64;
+    static constexpr int LDP = SWZ ? D : D + 4;    // [row][channel] row stride
     static constexpr int KS = D / 4;               // MFMA K-steps over d
     static constexpr int NTC = D / 16;             // 16-wide column tiles of d
     static constexpr int NWIN = T / 16;            // windows per sub-block
@@ -525,13 +530,15 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     // LDS pool (floats). Arrays that are dead in a phase lend their space:
     // the k rows (dead after the epilogue, until the update writes z) hold
     // the windows' L tables; the v rows (dead after the epilogue) hold the
-    // N and T' tables, and at a chunk end Q_L^T when it fits.
+    // N tables, the T' tables when they fit too, and at a chunk end Q_L^T
+    // when it fits.
     static constexpr int SZ_TOK = T * LDP;
     static constexpr int SZ_LC = NWIN * 16 * WS;
     static constexpr int SZ_NN = NWIN * 16 * WS;
     static constexpr int SZ_TP = NWIN * 256;
     static constexpr int SZ_QT = D * LDP;
-    static_assert(SZ_LC <= SZ_TOK && SZ_NN + SZ_TP <= SZ_TOK, "window tables fit");
+    static_assert(SZ_LC <= SZ_TOK && SZ_NN <= SZ_TOK, "window tables fit");
+    static constexpr bool TP_IN_ES = SZ_NN + SZ_TP <= SZ_TOK;
     static constexpr bool QT_IN_ES = SZ_QT <= SZ_TOK;
     // else, when it fits, over the x, k/z, v and k^ rows (contiguous), which
     // are dead at a chunk end once the readout has read the z rows
@@ -548,14 +555,16 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int O_GZ = O_GA + T;
     static constexpr int O_RB = O_GZ + T;
     static constexpr int O_WG = O_RB + T;
-    static constexpr int O_PI = O_WG + 4;
+    static constexpr int O_PI = O_WG + (NWIN + 3) / 4 * 4;
     static constexpr int O_XB = O_PI + T;
     static constexpr int SZ_XB = (JS == 2) ? 2 * NTC * 512 : 0;
     static constexpr int O_KZ2 = O_XB + SZ_XB;
     static constexpr int O_QV = O_KZ2 + ((JS == 2) ? SZ_TOK : 0);
-    static constexpr int O_QT = QT_IN_ES ? O_ES : QT_IN_TOK ? O_XS : O_QV + (HAS_Q ? SZ_TOK : 0);
-    static constexpr int POOL =
-        ((QT_IN_ES || QT_IN_TOK) ? O_QV : O_QT + SZ_QT) + (HAS_Q ? SZ_TOK : 0);
+    static constexpr int O_TPX = O_QV + (HAS_Q ? SZ_TOK : 0);     // T' tables, if not in v rows
+    static constexpr int O_TP = TP_IN_ES ? O_ES + SZ_NN : O_TPX;
+    static constexpr int O_QTX = O_TPX + (TP_IN_ES ? 0 : SZ_TP);  // Q_L^T, if on its own
+    static constexpr int O_QT = QT_IN_ES ? O_ES : QT_IN_TOK ? O_XS : O_QTX;
+    static constexpr int POOL = O_QTX + ((QT_IN_ES || QT_IN_TOK) ? 0 : SZ_QT);
 };
 
 // Index of T'[s][t] in a window's 16 x 16 table: rows of 16 floats, the four
@@ -564,6 +573,22 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
 __device__ __forceinline__ int tp_index(int s, int t)
 {
     return s * 16 + ((((t >> 2) ^ (s >> 1)) & 3) << 2) + (t & 3);
+}
+
+// Swizzle of the 16-byte blocks of row `row` in the unpadded [row][channel]
+// arrays of the scan kernel's long sub-blocks at d = 32: block b of the row
+// is stored at block b ^ swz_row(row).
+// Chosen with a model of the LDS banks (128-bit reads: 64 banks, 16 lanes a
+// cycle, a half-wave's quads split by the parity of the quad index; 128-bit
+// writes: 32 banks, 8 consecutive lanes; 32-bit accesses: 32 banks, 32
+// lanes) so that every row access of the scan kernel is free of bank
+// conflicts: 16 lanes on 16 rows at one column block, 16 rows at two column
+// blocks, 4 or 8 lanes per row on consecutive blocks, and 32-bit column
+// accesses of 4 rows x 16 channels.
+__device__ __forceinline__ int swz_row(int row)
+{
+    // [0, 4, 6, 2][(row >> 2) & 3] | (bit 0 ^ bit 1 of row)
+    return ((0x2640 >> (((row >> 2) & 3) << 2)) & 0xF) | ((row ^ (row >> 1)) & 1);
 }
 
 // 16-byte vector of input elements
@@ -685,7 +710,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const Lc = pool + Cfg::O_KZ;    // per window L [t][s] (window tables)
     float *const Es = pool + Cfg::O_ES;    // v rows (generation)
     float *const Nn = pool + Cfg::O_ES;    // per window N [t][s] (window tables, update)
-    float *const Tp = pool + Cfg::O_ES + Cfg::SZ_NN;   // per window T', tp_index layout
+    float *const Tp = pool + Cfg::O_TP;    // per window T', tp_index layout
     float *const KHa = pool + Cfg::O_KH;   // k^_t rows
     float *const Et = pool + Cfg::O_ET;    // e = k^ - v, [channel][token]
     float *const AL = pool + Cfg::O_AL;    // alpha_t (1 on padding tokens)
@@ -700,6 +725,25 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     float *const QVa = pool + Cfg::O_QV;   // separate query rows q_t (HAS_Q)
     float *const Qt = pool + Cfg::O_QT;    // Q_L^T at a chunk end
     const float *const QR = HAS_Q ? QVa : Xs;   // query rows
+    // Offset of element (row, c) of a [row][channel] array (x, k/z, v, k^,
+    // query and boundary rows, Q_L^T); c % 4 is kept, so aligned groups of 4
+    // channels stay contiguous.
+    auto ix = [](int row, int c) {
+        return row * LDP + (Cfg::SWZ ? (c ^ (swz_row(row) << 2)) : c);
+    };
+    // n consecutive channels c0.. (c0 % 4 == 0) of one row into registers
+    auto ldrow = [&](const float *base, int row, int c0, auto &r) {
+        constexpr int n = sizeof(r) / sizeof(float);
+        static_assert(n % 4 == 0, "whole 16-byte blocks");
+#pragma unroll
+        for (int k = 0; k < n / 4; ++k) {
+            const float4 v = ld4(base + ix(row, c0 + 4 * k));
+            r[4 * k] = v.x;
+            r[4 * k + 1] = v.y;
+            r[4 * k + 2] = v.z;
+            r[4 * k + 3] = v.w;
+        }
+    };
     // Token column of e in its [channel][token] layout, XOR-swizzled by the
     // epilogue lane that stores the channel: those lanes each store ECPL
     // consecutive channels of one token, and unswizzled the lanes of a
@@ -730,7 +774,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 
     const float *st = states + (static_cast<size_t>(r) * heads + h) * (ROWS * D);
     for (int idx = tid; idx < ROWS * D; idx += NT)
-        Bs[(idx / D) * LDP + idx % D] = st[idx];
+        Bs[ix(idx / D, idx % D)] = st[idx];
 
     const size_t xbase = static_cast<size_t>(b) * N * C + static_cast<size_t>(h) * D;
     uint4 pre[NPF], preq[NPF];
@@ -770,7 +814,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         for (int jl = 0; jl < NJ; ++jl)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                Qt[(16 * (jg * NJ + jl) + 4 * lk + i) * LDP + 16 * it + lm] = qacc[jl][i];
+                Qt[ix(16 * (jg * NJ + jl) + 4 * lk + i, 16 * it + lm)] = qacc[jl][i];
     };
     // With two waves per 16 rows of Q, every window ends in a block barrier
     // after the window's table reads, so Q_L^T can be staged at the end of the
@@ -806,9 +850,9 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 }
 #pragma unroll
                 for (int e = 0; e < VE / 4; ++e) {
-                    st4(Xs + u * LDP + sg * VE + 4 * e, f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
+                    st4(Xs + ix(u, sg * VE + 4 * e), f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
                     if (HAS_Q)
-                        st4(QVa + u * LDP + sg * VE + 4 * e, fq[4 * e], fq[4 * e + 1], fq[4 * e + 2],
+                        st4(QVa + ix(u, sg * VE + 4 * e), fq[4 * e], fq[4 * e + 1], fq[4 * e + 2],
                             fq[4 * e + 3]);
                 }
             }
@@ -837,14 +881,14 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         for (int tn = wave; tn < 2 * NTC; tn += NW) {
             float *dst = (tn < NTC) ? KZ : Es;
             const int oc = (tn % NTC) * 16 + lm;
-            const float *brow = Bs + (D + tn * 16 + lm) * LDP;
+            const int brow = D + tn * 16 + lm;   // boundary row of this lane
             if constexpr (std::is_same<InT, uint16_t>::value) {
                 constexpr int KB = D / 32;
                 bf16x8 bh[KB], bm[KB], bl[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     float bv[8];
-                    lds_load(brow + 32 * kb + 8 * lk, bv);
+                    ldrow(Bs, brow, 32 * kb + 8 * lk, bv);
                     split3_bf16(bv, bh[kb], bm[kb], bl[kb]);
                 }
                 // every token tile of the sub-block (rows past nt are zero)
@@ -854,7 +898,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
                         float xv[8];
-                        lds_load(Xs + (tm * 16 + lm) * LDP + 32 * kb + 8 * lk, xv);
+                        ldrow(Xs, tm * 16 + lm, 32 * kb + 8 * lk, xv);
                         xa[tm][kb] = pack_bf16_exact(xv);
                     }
 #pragma unroll
@@ -868,22 +912,22 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     }
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+                        dst[ix(tm * 16 + 4 * lk + rr, oc)] = acc[rr];
                 }
             } else {
                 float bg[KS];
-                lds_load(brow + lk * KS, bg);
+                ldrow(Bs, brow, lk * KS, bg);
 #pragma unroll
                 for (int tm = 0; tm < NWIN; ++tm) {
                     float a[KS];
-                    lds_load(Xs + (tm * 16 + lm) * LDP + lk * KS, a);
+                    ldrow(Xs, tm * 16 + lm, lk * KS, a);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
                         acc = mfma4(a[s], bg[s], acc);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        dst[(tm * 16 + 4 * lk + rr) * LDP + oc] = acc[rr];
+                        dst[ix(tm * 16 + 4 * lk + rr, oc)] = acc[rr];
                 }
             }
         }
@@ -897,11 +941,11 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             const int c0e = ep * ECPL;
             if (u < nt) {
                 float kk[ECPL], vv[ECPL], xv[ECPL], be[ECPL], ba[ECPL];
-                lds_load(KZ + u * LDP + c0e, kk);
-                lds_load(Es + u * LDP + c0e, vv);
-                lds_load(Xs + u * LDP + c0e, xv);
-                lds_load(Bs + 3 * D * LDP + c0e, be);
-                lds_load(Bs + (3 * D + 1) * LDP + c0e, ba);
+                ldrow(KZ, u, c0e, kk);
+                ldrow(Es, u, c0e, vv);
+                ldrow(Xs, u, c0e, xv);
+                ldrow(Bs, 3 * D, c0e, be);
+                ldrow(Bs, 3 * D + 1, c0e, ba);
                 float nk2 = 0.f, er = 0.f, ar = 0.f;
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c) {
@@ -924,7 +968,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 }
 #pragma unroll
                 for (int c4 = 0; c4 < ECPL / 4; ++c4)
-                    st4(KHa + u * LDP + c0e + 4 * c4, khv[4 * c4], khv[4 * c4 + 1], khv[4 * c4 + 2],
+                    st4(KHa + ix(u, c0e + 4 * c4), khv[4 * c4], khv[4 * c4 + 1], khv[4 * c4 + 2],
                         khv[4 * c4 + 3]);
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c)
@@ -961,7 +1005,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 // padding token: leaves Q unchanged
 #pragma unroll
                 for (int c4 = 0; c4 < ECPL / 4; ++c4)
-                    st4(KHa + u * LDP + c0e + 4 * c4, 0.f, 0.f, 0.f, 0.f);
+                    st4(KHa + ix(u, c0e + 4 * c4), 0.f, 0.f, 0.f, 0.f);
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c)
                     Et[(c0e + c) * ETS + et_col(c0e + c, u)] = 0.f;
@@ -981,8 +1025,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             v4f gkk = {0.f, 0.f, 0.f, 0.f}, gqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jt = 0; jt < NTC; ++jt) {
-                const float4 kv = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
-                const float4 qv = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                const float4 kv = ld4(KHa + ix(tb + lm, 16 * jt + 4 * lk));
+                const float4 qv = ld4(QR + ix(tb + lm, 16 * jt + 4 * lk));
                 gkk = mfma16(kv, kv, gkk);
                 gqk = mfma16(kv, qv, gqk);
             }
@@ -1122,8 +1166,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
                     const int jt = jg * NJ + jl;
-                    kv[jl] = ld4(KHa + (tb + lm) * LDP + 16 * jt + 4 * lk);
-                    qv[jl] = ld4(QR + (tb + lm) * LDP + 16 * jt + 4 * lk);
+                    kv[jl] = ld4(KHa + ix(tb + lm, 16 * jt + 4 * lk));
+                    qv[jl] = ld4(QR + ix(tb + lm, 16 * jt + 4 * lk));
                 }
             };
             if (nwin > 0)
@@ -1147,10 +1191,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
                     const int jt = jg * NJ + jl;
-                    kt[jl] = make_float4(KHa[(tb + 4 * lk) * LDP + 16 * jt + lm],
-                                         KHa[(tb + 4 * lk + 1) * LDP + 16 * jt + lm],
-                                         KHa[(tb + 4 * lk + 2) * LDP + 16 * jt + lm],
-                                         KHa[(tb + 4 * lk + 3) * LDP + 16 * jt + lm]);
+                    kt[jl] = make_float4(KHa[ix(tb + 4 * lk, 16 * jt + lm)],
+                                         KHa[ix(tb + 4 * lk + 1, 16 * jt + lm)],
+                                         KHa[ix(tb + 4 * lk + 2, 16 * jt + lm)],
+                                         KHa[ix(tb + 4 * lk + 3, 16 * jt + lm)]);
                 }
                 if (JS == 2) {
                     float *xb = XB + ((win & 1) * NTC + it) * 512 + 4 * lane;
@@ -1195,7 +1239,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 float *zd = (JS == 2 && jg == 1) ? KZ2 : KZ;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    zd[(tb + 4 * lk + i) * LDP + 16 * it + lm] = Z[i];
+                    zd[ix(tb + 4 * lk + i, 16 * it + lm)] = Z[i];
             }
             if constexpr (QT_EARLY) {
                 if (chunk_end && cend < N)
@@ -1227,10 +1271,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
             for (int tm = tm0; tm < nwin; tm += tms) {
                 float a[KS];
-                lds_load(KZ + (tm * 16 + lm) * LDP + lk * KS, a);
+                ldrow(KZ, tm * 16 + lm, lk * KS, a);
                 if (JS == 2) {
                     float a2[KS];
-                    lds_load(KZ2 + (tm * 16 + lm) * LDP + lk * KS, a2);
+                    ldrow(KZ2, tm * 16 + lm, lk * KS, a2);
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
                         a[s] += a2[s];
@@ -1240,7 +1284,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int tn = tn0; tn < NTC; tn += tns) {
                     float br[KS];
-                    lds_load(Bs + (tn * 16 + lm) * LDP + lk * KS, br);
+                    ldrow(Bs, tn * 16 + lm, lk * KS, br);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
@@ -1270,8 +1314,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                         break;
                     const int tm = tile / NTC, tn = tile % NTC;
                     float a[KS], bq[KS];
-                    lds_load(Bs + (tm * 16 + lm) * LDP + lk * KS, a);
-                    lds_load(Qt + (tn * 16 + lm) * LDP + lk * KS, bq);
+                    ldrow(Bs, tm * 16 + lm, lk * KS, a);
+                    ldrow(Qt, tn * 16 + lm, lk * KS, bq);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
@@ -1281,11 +1325,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 float vacc = 0.f;
                 const int vv = tid / D, vj = tid % D;
                 if (tid < 2 * D) {
-                    const float4 *br4 = reinterpret_cast<const float4 *>(Bs + (3 * D + vv) * LDP);
-                    const float4 *q4 = reinterpret_cast<const float4 *>(Qt + vj * LDP);
 #pragma unroll
                     for (int k = 0; k < D / 4; ++k) {
-                        const float4 bb = br4[k], qq = q4[k];
+                        const float4 bb = ld4(Bs + ix(3 * D + vv, 4 * k));
+                        const float4 qq = ld4(Qt + ix(vj, 4 * k));
                         vacc = fmaf(bb.x, qq.x, vacc);
                         vacc = fmaf(bb.y, qq.y, vacc);
                         vacc = fmaf(bb.z, qq.z, vacc);
@@ -1301,10 +1344,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     const int tm = tile / NTC, tn = tile % NTC;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        Bs[(tm * 16 + 4 * lk + rr) * LDP + tn * 16 + lm] = racc[w][rr];
+                        Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
                 }
                 if (tid < 2 * D)
-                    Bs[(3 * D + vv) * LDP + vj] = vacc;
+                    Bs[ix(3 * D + vv, vj)] = vacc;
             }
             reset_q();
         }
