@@ -686,12 +686,35 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
     }
 }
 
-template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT>
+// Per-chain record of the forward that the windowed backward reads (SAVE):
+// every chunk's boundary rows and closing Q_L, and every 16-token window's
+// opening Q_0 and its u_t rows (windows counted from each chunk start).
+// Chains are chain_floats apart; inside a chain the layout depends on the
+// route's chunk count nch and window slots per chunk nwc.
+struct FwdSave {
+    float *base = nullptr;
+    long long chain_floats = 0;
+};
+template <int D> struct SaveLayout {
+    static constexpr long long BR = (3LL * D + 2) * D;   // boundary rows
+    long long nch, nwc;
+    __host__ __device__ long long o_bnd(long long c) const { return c * BR; }
+    __host__ __device__ long long o_ql(long long c) const { return nch * BR + c * D * D; }
+    __host__ __device__ long long o_q0(long long c, long long w) const {
+        return nch * (BR + D * D) + (c * nwc + w) * D * D;
+    }
+    __host__ __device__ long long o_u(long long c, long long w) const {
+        return nch * (BR + D * D) + nch * nwc * D * D + (c * nwc + w) * 16 * D;
+    }
+    __host__ __device__ long long floats() const { return nch * (BR + D * D + nwc * (D * D + 16 * D)); }
+};
+
+template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false>
 __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
-    float eps, int chunk_row, int chunk_col, unsigned flags, int nchains)
+    float eps, int chunk_row, int chunk_col, unsigned flags, int nchains, FwdSave sv)
 {
     using Cfg = MCfg<D, NW, T, HAS_Q>;
     constexpr int NT = Cfg::NT, ROWS = Cfg::ROWS, LDP = Cfg::LDP, KS = Cfg::KS,
@@ -829,8 +852,17 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     int nt = (T < cend) ? T : cend;
     issue_loads(s0, nt);
 
+    float *const svc = SAVE ? sv.base + static_cast<long long>(chain) * sv.chain_floats : nullptr;
+    const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
     while (true) {
         __syncthreads();   // previous sub-block is done with every token array; Bs is current
+        if constexpr (SAVE) {
+            if (s0 == c0) {   // a chunk's boundary rows
+                float *dst = svc + sl.o_bnd(c0 / L);
+                for (int idx = tid; idx < ROWS * D; idx += NT)
+                    dst[idx] = Bs[ix(idx / D, idx % D)];
+            }
+        }
 
         // (1) store the prefetched tokens (zero rows past nt)
 #pragma unroll
@@ -1172,8 +1204,16 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             };
             if (nwin > 0)
                 load_rows(0);
+            auto save_q = [&](float *dst) {   // this wave's tiles of Q, row-major
+#pragma unroll
+                for (int jl = 0; jl < NJ; ++jl)
+                    *reinterpret_cast<float4 *>(dst + (16 * it + lm) * D + 16 * (jg * NJ + jl) + 4 * lk) =
+                        make_float4(qacc[jl][0], qacc[jl][1], qacc[jl][2], qacc[jl][3]);
+            };
             for (int win = 0; win < nwin; ++win) {
                 const int tb = 16 * win;
+                if constexpr (SAVE)
+                    save_q(svc + sl.o_q0(c0 / L, (s0 - c0) / 16 + win));
                 v4f A = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
@@ -1212,6 +1252,14 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 A[3] = fmaf(ga.w, A[3], ee.w);
                 v4f U = {0.f, 0.f, 0.f, 0.f};
                 U = mfma16(tpv, A, U);
+                if constexpr (SAVE) {   // u_t rows of the window (both column halves hold them)
+                    if (jg == 0) {
+                        float *du = svc + sl.o_u(c0 / L, (s0 - c0) / 16 + win);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            du[(4 * lk + rr) * D + 16 * it + lm] = U[rr];
+                    }
+                }
                 Z[0] *= gz.x;
                 Z[1] *= gz.y;
                 Z[2] *= gz.z;
@@ -1245,6 +1293,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 if (chunk_end && cend < N)
                     stage_qt();
             }
+            if constexpr (SAVE) {
+                if (chunk_end)
+                    save_q(svc + sl.o_ql(c0 / L));
+            }
         } else if constexpr (JS == 2) {
             // the update's per-window block barrier, for the waves outside it
             for (int win = 0; win < nwin; ++win)
@@ -1265,7 +1317,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     tm = w, w + NW, ... and writes whole output rows of its head;
         //     otherwise wave w takes the channel tiles tn = w, w + NW, ... for
         //     every token tile.
-        {
+        if constexpr (!SAVE) {
             constexpr bool BY_TOKENS = NW > NTC;
             const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
             const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
@@ -1518,6 +1570,7 @@ __global__ __launch_bounds__(256) void init_kernel(float *__restrict__ st, long 
 // ------------------------------------------------------------ backward pass
 
 #include "srnl_bwd.inc"
+#include "srnl_bwd_wy.inc"
 
 // ------------------------------------------------------------ host side
 
@@ -1602,9 +1655,12 @@ int longest_chunk(int H, int W, unsigned mask, int chunk_row, int chunk_col)
     return static_cast<int>(L);
 }
 
-template <int D, int T, typename InT>
+// With SAVE the kernel writes no route outputs but the record FwdSave sv
+// for the windowed backward (readout after the write only).
+template <int D, int T, typename InT, bool SAVE = false>
 void launch_scan_mfma(const void *x, const srnl_params *p, int B, int H, int W, int C,
-                      int heads, unsigned mask, int R, int nchains, int nblocks, float *out)
+                      int heads, unsigned mask, int R, int nchains, int nblocks, float *out,
+                      FwdSave sv = FwdSave())
 {
     constexpr int NW = MfmaNW<D, T>::value;
     hipStream_t st = static_cast<hipStream_t>(p->stream);
@@ -1613,14 +1669,18 @@ void launch_scan_mfma(const void *x, const srnl_params *p, int B, int H, int W, 
         hipLaunchKernelGGL(kern, dim3(nblocks), dim3(NW * 64), 0, st,
                            static_cast<const InT *>(x), static_cast<const InT *>(p->q),
                            p->states, out, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
-                           p->chunk_row, p->chunk_col, p->flags, nchains);
+                           p->chunk_row, p->chunk_col, p->flags, nchains, sv);
     };
-    if (before)
+    if constexpr (SAVE) {
+        has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT, true>)
+              : go(scan_mfma_kernel<D, NW, T, false, false, InT, true>);
+    } else if (before) {
         has_q ? go(scan_mfma_kernel<D, NW, T, true, true, InT>)
               : go(scan_mfma_kernel<D, NW, T, true, false, InT>);
-    else
+    } else {
         has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT>)
               : go(scan_mfma_kernel<D, NW, T, false, false, InT>);
+    }
 }
 
 template <int D, typename InT>
@@ -1694,10 +1754,15 @@ struct BwdLayout {
 
 long long align64(long long n) { return (n + 63) / 64 * 64; }
 
+// The windowed backward (d = 32, readout after the write) reads a record of
+// the forward instead of re-running it token by token.
+bool bwd_windowed(int d, const srnl_params *p) { return d == 32 && !(p->flags & F_READ_BEFORE); }
+
 BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask,
                      const srnl_params *p)
 {
     BwdLayout l;
+    const bool wy = bwd_windowed(d, p);
     const int R = popcount4(mask);
     const long long N = static_cast<long long>(H) * W;
     const long long rows = 3LL * d + 2;
@@ -1711,7 +1776,8 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
         if (L < 1)
             L = 1;
         const long long nch = (N + L - 1) / L;
-        const long long f = nch * rows * d + L * d * d + rows * d;
+        const long long f = wy ? SaveLayout<32>{nch, (L + 15) / 16}.floats()
+                               : nch * rows * d + L * d * d + rows * d;
         if (f > l.chain_floats)
             l.chain_floats = f;
     }
@@ -1740,11 +1806,47 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
                            dy, ws, l.chain_floats, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
                            p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
     };
-    if (p->flags & F_READ_BEFORE)
-        go(scan_bwd_kernel<D, true, InT>);
-    else
-        go(scan_bwd_kernel<D, false, InT>);
-    srnl_status s = launch_check("scan_bwd_kernel");
+    srnl_status s;
+    if constexpr (D == 32) {
+        if (bwd_windowed(D, p)) {
+            // the forward record, then the windowed backward
+            const int nblocks = (nchains + 7) / 8 * 8;
+            const FwdSave sv{ws, l.chain_floats};
+            const int L = longest_chunk(H, W, mask, p->chunk_row, p->chunk_col);
+            if (L <= 16)
+                launch_scan_mfma<D, 16, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
+                                                   nblocks, nullptr, sv);
+            else if (L <= 32)
+                launch_scan_mfma<D, 32, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
+                                                   nblocks, nullptr, sv);
+            else
+                launch_scan_mfma<D, 64, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
+                                                   nblocks, nullptr, sv);
+            s = launch_check("scan_mfma_kernel (forward record)");
+            if (s != SRNL_OK)
+                return s;
+            auto gw = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3(nblocks), dim3(wyb::NT), 0, st,
+                                   static_cast<const InT *>(x), static_cast<const InT *>(p->q), dy,
+                                   sv, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                                   p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
+            };
+            if (p->q)
+                gw(scan_bwd_wy_kernel<true, InT>);
+            else
+                gw(scan_bwd_wy_kernel<false, InT>);
+            s = launch_check("scan_bwd_wy_kernel");
+        } else {
+            go(scan_bwd_kernel<D, true, InT>);
+            s = launch_check("scan_bwd_kernel");
+        }
+    } else {
+        if (p->flags & F_READ_BEFORE)
+            go(scan_bwd_kernel<D, true, InT>);
+        else
+            go(scan_bwd_kernel<D, false, InT>);
+        s = launch_check("scan_bwd_kernel");
+    }
     if (s != SRNL_OK)
         return s;
     const long long n = static_cast<long long>(B) * H * W * C;

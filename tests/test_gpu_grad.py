@@ -114,6 +114,34 @@ def test_grad_d32_long_rows():
     run_case(_wl("glong", 1, 6, 40, 2, 32, seed=6, x_kind="ar1"))
 
 
+# d = 32 without FLAG_READ_BEFORE takes the windowed backward (a forward
+# record, then 16-token windows on MFMA); the same cases as above there.
+@pytest.mark.parametrize("flags", [0, srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
+                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE])
+def test_grad_variants_d32(flags):
+    std = 0.3 if flags == srnl.FLAG_NO_CAP else 1.0
+    run_case(_wl("gv32", 2, 5, 7, 2, 32, seed=40 + flags, state_std=std), flags=flags)
+
+
+def test_grad_stressed_inputs_d32():
+    run_case(_wl("gadv32", 1, 6, 9, 2, 32, seed=19, state_std=2.0, outlier_frac=0.1))
+
+
+@pytest.mark.parametrize("cr,cc", [(3, 2), (1, 1), (17, 0), (40, 5), (100, 100)])
+def test_grad_chunk_overrides_d32(cr, cc):
+    run_case(_wl("gch32", 1, 6, 23, 1, 32, seed=cr * 7 + cc, state_std=0.5,
+                 chunk_row=cr, chunk_col=cc))
+
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 6, 9])
+def test_grad_route_masks_d32(mask):
+    run_case(_wl("gm32", 2, 4, 6, 1, 32, seed=50 + mask), mask=mask)
+
+
+def test_grad_separate_queries_f32_d32():
+    run_case(_wl("gq32", 2, 5, 6, 2, 32, dtype="f32", seed=8, separate_q=True))
+
+
 def test_grad_is_deterministic():
     wl = _wl("gdet", 2, 5, 5, 2, 16, seed=3)
     a, _ = run_case(wl)
