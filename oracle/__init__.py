@@ -37,7 +37,8 @@ class _Opts(ctypes.Structure):
                 ("chunk_row", ctypes.c_int), ("chunk_col", ctypes.c_int),
                 ("cap_mode", ctypes.c_int), ("clamp", ctypes.c_int),
                 ("fixed_alpha", ctypes.c_int),
-                ("readout_before", ctypes.c_int)]
+                ("readout_before", ctypes.c_int),
+                ("freeze_kv", ctypes.c_int)]
 
 
 _lib = None
@@ -88,7 +89,7 @@ def scan(x, states, heads: int, d: int, route_mask: int = 15, q=None, *,
          alpha_max: float = 0.9, eps: float = 1e-6, chunk_row: int = 0,
          chunk_col: int = 0, cap_mode: int = CAP_SOFT, clamp: bool = True,
          fixed_alpha: bool = False, readout_before: bool = False,
-         trace: bool = False, threads: int = 1):
+         freeze_kv: bool = False, trace: bool = False, threads: int = 1):
     """Per-route outputs y [R][B][H*W][C] (traversal order) in float64.
 
     ``threads`` > 1 splits the batch over Python threads (each runs the
@@ -101,7 +102,7 @@ def scan(x, states, heads: int, d: int, route_mask: int = 15, q=None, *,
     R = bin(route_mask & 15).count("1")
     N = H * W
     opts = _Opts(alpha_max, eps, chunk_row, chunk_col, cap_mode, int(clamp),
-                 int(fixed_alpha), int(readout_before))
+                 int(fixed_alpha), int(readout_before), int(freeze_kv))
 
     def run(b0, b1):
         xs = np.ascontiguousarray(x[b0:b1])

@@ -57,10 +57,13 @@ def route_order(r: int, H: int, W: int) -> np.ndarray:
 def forward(x, states, scales, heads: int, d: int, route_mask: int = 15, q=None, *,
             alpha_max: float = 0.9, eps: float = 1e-6, chunk_row: int = 0,
             chunk_col: int = 0, cap_mode: int = CAP_SOFT, clamp: bool = True,
-            fixed_alpha: bool = False, readout_before: bool = False):
+            fixed_alpha: bool = False, readout_before: bool = False,
+            freeze_kv: bool = False):
     """x [B,H,W,C], states [4][heads][3d^2+2d], scales [4][C] (float64
     tensors; q like x or None). Returns (y [R][B][H*W][C] in traversal
-    order, fused [B,H,W,C])."""
+    order, fused [B,H,W,C]). ``freeze_kv`` writes only the content memory
+    (the frozen key/value and dynamics ablation, [SUMMARY ablation
+    paragraph])."""
     B, H, W, C = x.shape
     N = H * W
     routes = [r for r in range(4) if (route_mask >> r) & 1]
@@ -122,7 +125,8 @@ def forward(x, states, scales, heads: int, d: int, route_mask: int = 15, q=None,
             ys.append(torch.einsum("rbhij,rbhj->rbhi", M[..., :d, :], qt))
         w = torch.einsum("rbhij,rbhj->rbhi", Bn, e)      # B e, every row
         s = torch.einsum("rbhij,rbhj->rbhi", M, kh) + w  # M k^ + B e
-        M = alpha[..., None, None] * M - eta2[..., None, None] * s[..., None] * kh[..., None, :]
+        Mw = alpha[..., None, None] * M - eta2[..., None, None] * s[..., None] * kh[..., None, :]
+        M = torch.cat([Mw[..., :d, :], M[..., d:, :]], dim=-2) if freeze_kv else Mw
         if not readout_before:
             ys.append(torch.einsum("rbhij,rbhj->rbhi", M[..., :d, :], qt))
     y = torch.stack(ys, dim=2).reshape(R, B, N, C)

@@ -71,8 +71,11 @@
  *
  * Variants (ablations named on the pages): hard injection clamp
  * min(eta, (1-alpha)/g) instead of the soft cap, no cap, no spectral
- * clamp [SUMMARY ablation paragraph]; fixed retention alpha = alpha_max and
- * readout before the write (alternative readings).
+ * clamp, and frozen key/value and dynamics memories [SUMMARY ablation
+ * paragraph]; fixed retention alpha = alpha_max and readout before the
+ * write (alternative readings). With the memories frozen only the content
+ * memory M_c is written; M_k, M_v, m_eta and m_alpha keep their initial
+ * values for the whole scan, so every chunk generates from them.  (READING)
  */
 #include <math.h>
 #include <stddef.h>
@@ -175,10 +178,11 @@ static void generate(const double *bnd, int d, const double *xt,
         g->w[r] = dot(bnd + (size_t)r * d, g->e, d);
 }
 
-/* One retained-DGD step on all 3d+2 working rows. */
-static void write_token(double *mem, int d, const token_gen *g)
+/* One retained-DGD step on the working rows: all 3d+2, or only the d rows
+ * of M_c when the other memories are frozen. */
+static void write_token(double *mem, int d, const token_gen *g, int freeze_kv)
 {
-    int rows = 3 * d + 2;
+    int rows = freeze_kv ? d : 3 * d + 2;
     for (int r = 0; r < rows; ++r) {
         double *m = mem + (size_t)r * d;
         double s = dot(m, g->khat, d) + g->w[r];  /* M k^ + B e */
@@ -256,7 +260,7 @@ int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
                         if (o->readout_before)
                             for (int a = 0; a < d; ++a)
                                 yt[a] = dot(mem + (size_t)a * d, qt, d);
-                        write_token(mem, d, &gen[u]);
+                        write_token(mem, d, &gen[u], o->freeze_kv);
                         if (!o->readout_before)
                             for (int a = 0; a < d; ++a)
                                 yt[a] = dot(mem + (size_t)a * d, qt, d);

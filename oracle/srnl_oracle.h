@@ -29,6 +29,7 @@ typedef struct {
     int clamp;          /* 1: spectral clamp on */
     int fixed_alpha;    /* 1: alpha = alpha_max */
     int readout_before; /* 1: y_t read before token t's write */
+    int freeze_kv;      /* 1: only M_c is written; M_k, M_v, m_eta, m_alpha stay */
 } srnl_oracle_opts;
 
 void srnl_oracle_route_index(int r, int H, int W, long t, int *i, int *j);

@@ -27,6 +27,7 @@ VARIANTS = [
     dict(clamp=False),
     dict(readout_before=True),
     dict(fixed_alpha=True),
+    dict(freeze_kv=True, chunk_row=2, chunk_col=5),
 ]
 
 

@@ -148,9 +148,10 @@ def _sig(z):
 
 
 def brute_force(x, st, heads, d, route_mask, q=None, alpha_max=0.9, eps=1e-6,
-                chunk_row=0, chunk_col=0, cap="soft", clamp=True):
+                chunk_row=0, chunk_col=0, cap="soft", clamp=True, freeze=False):
     """Dense extended-precision restatement: per token build R and G as
-    matrices and apply M <- M R - eta'' G to every memory (vectors as 1 x d)."""
+    matrices and apply M <- M R - eta'' G to every memory (vectors as 1 x d);
+    with ``freeze`` only to the content memory."""
     B, H, W, C = x.shape
     N = H * W
     X = x.reshape(B, N, C).astype(LD)
@@ -193,7 +194,7 @@ def brute_force(x, st, heads, d, route_mask, q=None, alpha_max=0.9, eps=1e-6,
                         n2 = kh @ kh
                         eta2 = min(eta1, 2 * alpha / n2) if (clamp and n2 > 0) else eta1
                         R = alpha * I - eta2 * np.outer(kh, kh)
-                        for i in range(5):
+                        for i in range(1 if freeze else 5):
                             G = np.outer(Bs[i] @ kh - Bs[i] @ v, kh)
                             mems[i] = mems[i] @ R - eta2 * G
                         y[b, t, sl] = mems[0] @ Qx[b, order[t], sl]
@@ -251,6 +252,46 @@ def test_brute_force_variants(cap, clamp):
                      chunk_col=5).astype(np.float64)
     scale = np.abs(yb).max()
     assert np.abs(y - yb).max() <= 1e-11 * scale
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 0])
+def test_brute_force_frozen_memories(chunk):
+    """Frozen key/value and dynamics memories [SUMMARY ablation paragraph]:
+    only M_c is written, so every chunk generates from the initial states."""
+    d, heads = 4, 2
+    x, st = _wl(3, 4, d=d, heads=heads, seed=21, std=1.0, B=1)
+    x = x * 2.0
+    y = oracle.scan(x, st, heads, d, 15, chunk_row=chunk, chunk_col=chunk, freeze_kv=True)
+    yb = brute_force(x, st, heads, d, 15, chunk_row=chunk, chunk_col=chunk,
+                     freeze=True).astype(np.float64)
+    scale = np.abs(yb).max()
+    assert np.abs(y - yb).max() <= 1e-12 * scale
+    # the ablation changes the output once there is more than one chunk
+    yf = oracle.scan(x, st, heads, d, 15, chunk_row=chunk, chunk_col=chunk)
+    assert np.abs(y - yf).max() > 1e-3 * scale
+
+
+def test_frozen_memories_keep_their_norms_and_single_chunk_is_unchanged():
+    """With frozen memories the traced norms of M_k, M_v, m_eta, m_alpha stay
+    at their initial values on every token; with one chunk per route the
+    frozen rows are only ever read at the first boundary, so the output
+    equals the full operator's."""
+    d, heads = 4, 2
+    x, st = _wl(3, 5, d=d, heads=heads, seed=22, std=1.0, B=2)
+    _, tr = oracle.scan(x, st, heads, d, 15, freeze_kv=True, trace=True)
+    dd = d * d
+    for slot, r in enumerate(range(4)):
+        for h in range(heads):
+            s = st[r, h]
+            init = [np.linalg.norm(s[dd:2 * dd]), np.linalg.norm(s[2 * dd:3 * dd]),
+                    np.linalg.norm(s[3 * dd:3 * dd + d]), np.linalg.norm(s[3 * dd + d:])]
+            for m in range(4):
+                assert np.allclose(tr[slot, :, h, :, 1 + m], init[m], rtol=1e-14, atol=0)
+                assert np.allclose(tr[slot, :, h, :, 6 + m], init[m], rtol=1e-14, atol=0)
+    N = 15
+    y1 = oracle.scan(x, st, heads, d, 15, chunk_row=N, chunk_col=N, freeze_kv=True)
+    y2 = oracle.scan(x, st, heads, d, 15, chunk_row=N, chunk_col=N)
+    assert np.array_equal(y1, y2)
 
 
 def test_separate_queries_brute_force():
