@@ -68,6 +68,8 @@ typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
 #define SRNL_FLAG_NO_CLAMP     0x4u  /* no spectral clamp */
 #define SRNL_FLAG_FIXED_ALPHA  0x8u  /* alpha = alpha_max for every token */
 #define SRNL_FLAG_READ_BEFORE  0x10u /* y_t read before token t's write */
+#define SRNL_FLAG_FREEZE_KV    0x20u /* only M_c is written; M_k, M_v, m_eta, m_alpha keep
+                                        their initial values (frozen key/value and dynamics) */
 
 /* Floats of initial state per (route, head): 3d^2 + 2d. */
 #define SRNL_STATE_FLOATS(d) (3 * (d) * (d) + 2 * (d))

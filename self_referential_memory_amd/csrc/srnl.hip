@@ -152,7 +152,7 @@ template <int D> struct ScanCfg {
 
 enum : unsigned {
     F_HARD_CAP = 0x1u, F_NO_CAP = 0x2u, F_NO_CLAMP = 0x4u, F_FIXED_ALPHA = 0x8u,
-    F_READ_BEFORE = 0x10u
+    F_READ_BEFORE = 0x10u, F_FREEZE_KV = 0x20u
 };
 
 template <int D, typename InT>
@@ -355,12 +355,14 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
                     Qm[qrow * LDP + part * CPL + c] = P[c];
             }
             __syncthreads();
+            // frozen key/value and dynamics memories: only M_c is refreshed
+            const int nref = (flags & F_FREEZE_KV) ? D * D : ROWS * D;
             float acc[NREF];
 #pragma unroll
             for (int k = 0; k < NREF; ++k) {
                 const int idx = tid + k * NT;
                 float a = 0.0f;
-                if (idx < ROWS * D) {
+                if (idx < nref) {
                     const int rr = idx / D, jj = idx % D;
                     const float *brow = Bs + rr * LDP;
 #pragma unroll 8
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
 #pragma unroll
             for (int k = 0; k < NREF; ++k) {
                 const int idx = tid + k * NT;
-                if (idx < ROWS * D)
+                if (idx < nref)
                     Bs[(idx / D) * LDP + idx % D] = acc[k];
             }
 #pragma unroll
@@ -1358,6 +1360,9 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                         stage_qt();
                     __syncthreads();
                 }
+                // frozen key/value and dynamics memories: only the M_c
+                // tiles (rows < D) and no vector memory are refreshed
+                const bool frz = (flags & F_FREEZE_KV) != 0;
                 v4f racc[RTW];
 #pragma unroll
                 for (int w = 0; w < RTW; ++w) {
@@ -1365,6 +1370,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     if (RT % NW != 0 && tile >= RT)
                         break;
                     const int tm = tile / NTC, tn = tile % NTC;
+                    if (frz && tm >= NTC)
+                        break;
                     float a[KS], bq[KS];
                     ldrow(Bs, tm * 16 + lm, lk * KS, a);
                     ldrow(Qt, tn * 16 + lm, lk * KS, bq);
@@ -1376,7 +1383,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 }
                 float vacc = 0.f;
                 const int vv = tid / D, vj = tid % D;
-                if (tid < 2 * D) {
+                if (tid < 2 * D && !frz) {
 #pragma unroll
                     for (int k = 0; k < D / 4; ++k) {
                         const float4 bb = ld4(Bs + ix(3 * D + vv, 4 * k));
@@ -1394,11 +1401,13 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     if (RT % NW != 0 && tile >= RT)
                         break;
                     const int tm = tile / NTC, tn = tile % NTC;
+                    if (frz && tm >= NTC)
+                        break;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
                         Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
                 }
-                if (tid < 2 * D)
+                if (tid < 2 * D && !frz)
                     Bs[ix(3 * D + vv, vj)] = vacc;
             }
             reset_q();
@@ -1901,7 +1910,7 @@ srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsign
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x1Fu)
+    if (p->flags & ~0x3Fu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
@@ -1969,7 +1978,7 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x1Fu)
+    if (p->flags & ~0x3Fu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");

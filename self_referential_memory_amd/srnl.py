@@ -21,6 +21,7 @@ SRNL_OK, SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE, SRNL_ER
 SRNL_F32, SRNL_BF16 = 0, 1
 FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = (
     0x1, 0x2, 0x4, 0x8, 0x10)
+FLAG_FREEZE_KV = 0x20
 
 EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",

@@ -76,6 +76,7 @@ def _scan(x=0, B=1, H=2, W=2, C=8, heads=2, d=4, mask=15, **kw):
     (dict(eps=float("inf")), srnl.SRNL_ERR_ARG),
     (dict(chunk_row=-1), srnl.SRNL_ERR_ARG),
     (dict(flags=0x100), srnl.SRNL_ERR_ARG),
+    (dict(flags=0x40), srnl.SRNL_ERR_ARG),          # first bit above the known flags
     (dict(in_dtype=7), srnl.SRNL_ERR_DTYPE),
     (dict(B=1 << 30, H=1 << 15, W=1 << 15, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # overflow
     (dict(B=1, H=1 << 16, W=1 << 16, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # H*W > INT_MAX

@@ -26,7 +26,8 @@ def _kw(wl, flags):
                 chunk_col=wl.chunk_col, cap_mode=_CAP[flags & 0x3],
                 clamp=not (flags & srnl.FLAG_NO_CLAMP),
                 fixed_alpha=bool(flags & srnl.FLAG_FIXED_ALPHA),
-                readout_before=bool(flags & srnl.FLAG_READ_BEFORE))
+                readout_before=bool(flags & srnl.FLAG_READ_BEFORE),
+                freeze_kv=bool(flags & srnl.FLAG_FREEZE_KV))
 
 
 def rel(g, o):
@@ -83,7 +84,8 @@ def test_grad_tiny_workload():
 
 
 @pytest.mark.parametrize("flags", [srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
-                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE])
+                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE,
+                                   srnl.FLAG_FREEZE_KV])
 def test_grad_variants(flags):
     std = 0.3 if flags == srnl.FLAG_NO_CAP else 1.0
     run_case(_wl("gv", 2, 4, 5, 2, 16, seed=flags, state_std=std), flags=flags)
@@ -117,7 +119,9 @@ def test_grad_d32_long_rows():
 # d = 32 without FLAG_READ_BEFORE takes the windowed backward (a forward
 # record, then 16-token windows on MFMA); the same cases as above there.
 @pytest.mark.parametrize("flags", [0, srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
-                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE])
+                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE,
+                                   srnl.FLAG_FREEZE_KV,
+                                   srnl.FLAG_FREEZE_KV | srnl.FLAG_READ_BEFORE])
 def test_grad_variants_d32(flags):
     std = 0.3 if flags == srnl.FLAG_NO_CAP else 1.0
     run_case(_wl("gv32", 2, 5, 7, 2, 32, seed=40 + flags, state_std=std), flags=flags)

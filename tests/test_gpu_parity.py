@@ -71,7 +71,8 @@ def oracle_forward(wl, bs=None, route_mask=None, flags=0, threads=8):
               chunk_col=wl.chunk_col, cap_mode=_CAP[flags & 0x3],
               clamp=not (flags & srnl.FLAG_NO_CLAMP),
               fixed_alpha=bool(flags & srnl.FLAG_FIXED_ALPHA),
-              readout_before=bool(flags & srnl.FLAG_READ_BEFORE))
+              readout_before=bool(flags & srnl.FLAG_READ_BEFORE),
+              freeze_kv=bool(flags & srnl.FLAG_FREEZE_KV))
 
     def job(br):
         b, r = br
@@ -276,7 +277,7 @@ def test_route_subsets(mask):
 
 @pytest.mark.parametrize("flags", [0, srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
                                    srnl.FLAG_FIXED_ALPHA, srnl.FLAG_READ_BEFORE,
-                                   srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP])
+                                   srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP, srnl.FLAG_FREEZE_KV])
 def test_variants_on_adversarial_inputs(flags):
     # large state spread and x50 outlier tokens: the cap and the clamp bind.
     # Without the cap these inputs are expansive (memory norms grow ~6e15x
@@ -319,12 +320,13 @@ SUB_BLOCK_VARIANTS = [
     (srnl.FLAG_READ_BEFORE, "f32", True),
     (srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP, "f32", False),
     (srnl.FLAG_FIXED_ALPHA, "bf16", True),
+    (srnl.FLAG_FREEZE_KV, "bf16", False),
 ]
 
 
 @pytest.mark.parametrize("grid", SUB_BLOCK_GRIDS, ids=[g[0] for g in SUB_BLOCK_GRIDS])
 @pytest.mark.parametrize("variant", SUB_BLOCK_VARIANTS, ids=["plain", "before_q", "hardcap_noclamp",
-                                                              "fixedalpha_q"])
+                                                              "fixedalpha_q", "freeze"])
 def test_sub_block_configurations(grid, variant):
     name, B, H, W, d, heads, cr, cc, std, outl = grid
     flags, dtype, q = variant
