@@ -519,7 +519,12 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int ECPL = D / EPL;           // channels per epilogue lane
     static constexpr int TE = T > 32 ? T : 32;     // token columns of the e rows
     static constexpr int ETS = TE + 4;             // [channel][token] row stride
-    static constexpr int WS = 20;                  // row stride of the per-window N and L tables
+    static constexpr int WS = 20;                  // row stride of the per-window L tables
+    // row stride of the per-window N tables: as WS, except with separate
+    // queries in the long sub-blocks at d = 32, where unpadded rows let the T'
+    // tables share the v rows and keep the footprint within half a CU's LDS
+    // (two chains per CU) at the cost of 2-way conflicts on one read per window
+    static constexpr int NS = (HAS_Q && SWZ) ? 16 : WS;
     static constexpr int JS = (NW >= 2 * NTC) ? 2 : 1;   // waves sharing 16 rows of Q
     static constexpr int NJ = NTC / JS;            // 16-column tiles of Q per wave
     static constexpr int CW = NTC * JS;            // waves in the token-order update
@@ -536,7 +541,7 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     // when it fits.
     static constexpr int SZ_TOK = T * LDP;
     static constexpr int SZ_LC = NWIN * 16 * WS;
-    static constexpr int SZ_NN = NWIN * 16 * WS;
+    static constexpr int SZ_NN = NWIN * 16 * NS;
     static constexpr int SZ_TP = NWIN * 256;
     static constexpr int SZ_QT = D * LDP;
     static_assert(SZ_LC <= SZ_TOK && SZ_NN <= SZ_TOK, "window tables fit");
@@ -720,7 +725,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 {
     using Cfg = MCfg<D, NW, T, HAS_Q>;
     constexpr int NT = Cfg::NT, ROWS = Cfg::ROWS, LDP = Cfg::LDP, KS = Cfg::KS,
-                  NTC = Cfg::NTC, ETS = Cfg::ETS, WS = Cfg::WS, JS = Cfg::JS, NJ = Cfg::NJ,
+                  NTC = Cfg::NTC, ETS = Cfg::ETS, WS = Cfg::WS, NS = Cfg::NS, JS = Cfg::JS, NJ = Cfg::NJ,
                   CW = Cfg::CW, NWIN = Cfg::NWIN;
     constexpr int VE = InVec<InT>::VE;
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
@@ -1120,7 +1125,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 Nr[i] = BEFORE ? (lt ? P[i] * gqk[i] : 0.0f) : Rr[i] * gqk[i];
             }
             st4(lc + t * WS + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
-            st4(Nn + win * 16 * WS + t * WS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
+            st4(Nn + win * 16 * NS + t * NS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
             if (t == 15)
                 st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
             if (lk == 0) {
@@ -1227,7 +1232,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 const float4 rb = ld4(RB + tb + 4 * lk);
                 const float4 ee = ld4(Et + (16 * it + lm) * ETS + et_col(16 * it + lm, tb + 4 * lk));
                 const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
-                const float4 nnv = ld4(Nn + win * 16 * WS + lm * WS + 4 * lk);
+                const float4 nnv = ld4(Nn + win * 16 * NS + lm * NS + 4 * lk);
                 const float wg = WG[win];
                 float4 kt[NJ];
 #pragma unroll
@@ -1361,7 +1366,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     __syncthreads();
                 }
                 // frozen key/value and dynamics memories: only the M_c
-                // tiles (rows < D) and no vector memory are refreshed
+                // tiles (rows < D) and no vector memory are stored back
                 const bool frz = (flags & F_FREEZE_KV) != 0;
                 v4f racc[RTW];
 #pragma unroll
@@ -1370,8 +1375,6 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     if (RT % NW != 0 && tile >= RT)
                         break;
                     const int tm = tile / NTC, tn = tile % NTC;
-                    if (frz && tm >= NTC)
-                        break;
                     float a[KS], bq[KS];
                     ldrow(Bs, tm * 16 + lm, lk * KS, a);
                     ldrow(Qt, tn * 16 + lm, lk * KS, bq);
@@ -1401,11 +1404,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     if (RT % NW != 0 && tile >= RT)
                         break;
                     const int tm = tile / NTC, tn = tile % NTC;
-                    if (frz && tm >= NTC)
-                        break;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
+                        if (!frz || tm < NTC)
+                            Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
                 }
                 if (tid < 2 * D && !frz)
                     Bs[ix(3 * D + vv, vj)] = vacc;
