@@ -47,6 +47,7 @@ STREAM_STATES = 2
 STREAM_SCALES = 3
 STREAM_OUTLIERS = 4
 STREAM_Q = 5
+STREAM_BLOCK = 6
 
 
 def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
@@ -135,6 +136,56 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     words = r.astype(np.uint16)
     vals = (words.astype(np.uint32) << np.uint32(16)).view(np.float32)
     return vals, words
+
+
+@dataclasses.dataclass
+class BlockWeights:
+    """Parameters of one residual block around the operator: layer norms,
+    the shared query projection, the 3x3 depthwise convolution and the
+    feed-forward network. The three projection matrices are bf16 values
+    (kept as fp32 arrays that are exactly representable in bf16); everything
+    else is fp32."""
+    ln1_w: np.ndarray   # [C]
+    ln1_b: np.ndarray   # [C]
+    wq: np.ndarray      # [C][C]  q = u wq^T
+    dw_w: np.ndarray    # [C][3][3]
+    dw_b: np.ndarray    # [C]
+    ln2_w: np.ndarray   # [C]
+    ln2_b: np.ndarray   # [C]
+    w1: np.ndarray      # [F][C]
+    b1: np.ndarray      # [F]
+    w2: np.ndarray      # [C][F]
+    b2: np.ndarray      # [C]
+    ln_eps: float = 1e-5
+
+    @property
+    def F(self) -> int:
+        return self.w1.shape[0]
+
+
+def block_weights(seed: int, C: int, F: int) -> BlockWeights:
+    """Seeded block parameters, all from the BLOCK stream in a fixed order:
+    norm gains 1 + 0.1 z, biases 0.1 z, projections z / sqrt(fan-in)
+    (rounded to bf16), depthwise taps z / 3."""
+    sizes = [C, C, C * C, 9 * C, C, C, C, F * C, F, C * F, C]
+    z = normals(seed, STREAM_BLOCK, sum(sizes))
+    parts, o = [], 0
+    for n in sizes:
+        parts.append(z[o:o + n])
+        o += n
+    f32 = np.float32
+    return BlockWeights(
+        ln1_w=(1.0 + 0.1 * parts[0]).astype(f32),
+        ln1_b=(0.1 * parts[1]).astype(f32),
+        wq=round_bf16((parts[2] / math.sqrt(C)).astype(f32).reshape(C, C))[0],
+        dw_w=(parts[3] / 3.0).astype(f32).reshape(C, 3, 3),
+        dw_b=(0.1 * parts[4]).astype(f32),
+        ln2_w=(1.0 + 0.1 * parts[5]).astype(f32),
+        ln2_b=(0.1 * parts[6]).astype(f32),
+        w1=round_bf16((parts[7] / math.sqrt(C)).astype(f32).reshape(F, C))[0],
+        b1=(0.1 * parts[8]).astype(f32),
+        w2=round_bf16((parts[9] / math.sqrt(F)).astype(f32).reshape(C, F))[0],
+        b2=(0.1 * parts[10]).astype(f32))
 
 
 @dataclasses.dataclass
