@@ -33,6 +33,7 @@
 #define SRNL_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -212,6 +213,52 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y_routes, int B, int H
                           int C, unsigned route_mask, const float *scales,
                           float *dy_routes, float *dscales, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * srnl_block_fwd -- one residual block around the operator [SUMMARY
+ * paragraph on 2-D maps: a two-branch residual of a depthwise convolution
+ * and SRNL, then a feed-forward network; OVERVIEW Four-Directional Scanning
+ * and Spatial Chunking: one shared query projection supplies the readout
+ * queries of every route, and the residual blocks hold projections,
+ * normalisation, a depthwise convolution and a feed-forward network]:
+ *   u   = LN1(x)                         per-token layer norm over C
+ *   q   = u wq^T                         shared query projection, no bias
+ *   s   = srnl_fuse(srnl_scan_fwd(u; q), scales)
+ *   h   = x + DWConv3x3(u) + s           zero padding, with bias
+ *   out = h + w2 GELU(w1 LN2(h) + b1) + b2   exact (erf) GELU
+ * LN(z) = (z - mean) / sqrt(var + ln_eps) * gain + bias, biased variance.
+ *   x, out  [B][H][W][C] in params->in_dtype (bf16 out is rounded to
+ *           nearest even); the operator runs on u and q in fp32 with every
+ *           other field of params (states, alpha_max, eps, chunks, flags,
+ *           stream); params->q must be NULL.
+ *   C in {32, 64, 128, 192, 256}; ffn_hidden F a positive multiple of 32.
+ *   wq, w1, w2 are bf16 words; the products are formed exactly from them
+ *   and fp32 activations, accumulated in fp32.
+ *   workspace: caller-owned device memory of srnl_block_workspace_bytes
+ *   (u, q, s and the route outputs, all fp32).
+ * Every pointer must be device memory, 16-byte aligned. Errors:
+ * SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE,
+ * SRNL_ERR_HIP.
+ */
+typedef struct {
+    const float *ln1_w, *ln1_b;      /* [C] gain and bias of LN1 */
+    const uint16_t *wq;              /* [C][C] bf16 */
+    const float *dw_w, *dw_b;        /* [C][3][3] taps (row offset, column offset), [C] */
+    const float *ln2_w, *ln2_b;      /* [C] */
+    const uint16_t *w1;              /* [F][C] bf16 */
+    const float *b1;                 /* [F] */
+    const uint16_t *w2;              /* [C][F] bf16 */
+    const float *b2;                 /* [C] */
+    const float *scales;             /* [4][C] route fusion scales (as srnl_fuse) */
+    int ffn_hidden;                  /* F */
+    float ln_eps;                    /* > 0 */
+} srnl_block_weights;
+
+size_t srnl_block_workspace_bytes(int B, int H, int W, int C, unsigned route_mask);
+srnl_status srnl_block_fwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                           unsigned route_mask, const srnl_params *params,
+                           const srnl_block_weights *weights, void *workspace,
+                           size_t workspace_bytes, void *out);
 
 /*
  * srnl_route_gather -- the route traversal as a standalone copy [OVERVIEW

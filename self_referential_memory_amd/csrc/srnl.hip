@@ -1919,6 +1919,27 @@ srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsign
     return SRNL_OK;
 }
 
+#include "srnl_block.inc"
+
+// Workspace of srnl_block_fwd (floats, 64-float aligned parts): u, q and the
+// fused operator output s ([B][H][W][C] each), then the route outputs
+// [R][B][H*W][C].
+struct BlockLayout {
+    long long plane = 0, o_q = 0, o_s = 0, o_y = 0, total = 0;
+};
+BlockLayout block_layout(int B, int H, int W, int C, unsigned mask)
+{
+    BlockLayout l;
+    l.plane = align64(static_cast<long long>(B) * H * W * C);
+    l.o_q = l.plane;
+    l.o_s = 2 * l.plane;
+    l.o_y = 3 * l.plane;
+    l.total = l.o_y + align64(static_cast<long long>(popcount4(mask)) * B * H * W * C);
+    return l;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI
@@ -2111,6 +2132,68 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W
     hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C, 256)), dim3(256), 0, st, part,
                        dscales, C, route_mask, static_cast<int>(nblk));
     return launch_check("fuse_bwd_scales_kernel");
+}
+
+size_t srnl_block_workspace_bytes(int B, int H, int W, int C, unsigned route_mask)
+{
+    long long n = 0;
+    if (check_grid(B, H, W, C, route_mask, &n) != SRNL_OK || n == 0)
+        return 0;
+    return static_cast<size_t>(block_layout(B, H, W, C, route_mask).total) * sizeof(float);
+}
+
+srnl_status srnl_block_fwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                           unsigned route_mask, const srnl_params *p,
+                           const srnl_block_weights *w, void *workspace, size_t workspace_bytes,
+                           void *out)
+{
+    g_last_error.clear();
+    long long n = 0;
+    srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
+    if (s != SRNL_OK)
+        return s;
+    if (!w)
+        return fail(SRNL_ERR_PTR, "block weights are NULL");
+    if (p->q)
+        return fail(SRNL_ERR_ARG, "the block forms its own queries: params->q must be NULL");
+    if (C != 32 && C != 64 && C != 128 && C != 192 && C != 256)
+        return fail(SRNL_ERR_ARG, "block channels must be 32, 64, 128, 192 or 256");
+    if (w->ffn_hidden < 32 || w->ffn_hidden % 32 != 0 || w->ffn_hidden > (1 << 16))
+        return fail(SRNL_ERR_ARG, "ffn_hidden must be a positive multiple of 32, at most 65536");
+    if (!(w->ln_eps > 0.0f) || !std::isfinite(w->ln_eps))
+        return fail(SRNL_ERR_ARG, "ln_eps must be positive and finite");
+    if (n == 0)
+        return SRNL_OK;
+    const BlockLayout l = block_layout(B, H, W, C, route_mask);
+    if (!workspace || workspace_bytes < static_cast<size_t>(l.total) * sizeof(float))
+        return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_block_workspace_bytes");
+    const void *ptrs[] = {x, out, workspace, p->states, w->ln1_w, w->ln1_b, w->wq, w->dw_w,
+                          w->dw_b, w->ln2_w, w->ln2_b, w->w1, w->b1, w->w2, w->b2, w->scales};
+    for (const void *q : ptrs)
+        if (!is_device_ptr(q))
+            return fail(SRNL_ERR_PTR, "x, out, workspace, states and every block weight must be device memory");
+    for (const void *q : ptrs)
+        if (!aligned16(q))
+            return fail(SRNL_ERR_PTR, "x, out, workspace, states and every block weight must be 16-byte aligned");
+    const long long ntok = static_cast<long long>(B) * H * W;
+    float *u = static_cast<float *>(workspace), *q = u + l.o_q, *sf = u + l.o_s, *y = u + l.o_y;
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    const bool bf = p->in_dtype == SRNL_BF16;
+    s = bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, nullptr, nullptr, st, true)
+           : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, nullptr, nullptr, st, true);
+    if (s != SRNL_OK)
+        return s;
+    srnl_params ps = *p;   // the operator reads u (fp32) with queries q
+    ps.q = q;
+    ps.in_dtype = SRNL_F32;
+    s = dispatch_scan<float>(d, u, &ps, B, H, W, C, heads, route_mask, y);
+    if (s != SRNL_OK)
+        return s;
+    s = srnl_fuse(y, B, H, W, C, route_mask, w->scales, SRNL_F32, sf, p->stream);
+    if (s != SRNL_OK)
+        return s;
+    return bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, sf, out, st, false)
+              : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, sf, out, st, false);
 }
 
 srnl_status srnl_route_gather(const void *x, int B, int H, int W, int C, unsigned route_mask,

@@ -25,7 +25,8 @@ FLAG_FREEZE_KV = 0x20
 
 EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
-           "srnl_route_gather", "srnl_init_states",
+           "srnl_route_gather", "srnl_init_states", "srnl_block_fwd",
+           "srnl_block_workspace_bytes",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
            "srnl_last_error")
 
@@ -42,6 +43,17 @@ class Params(ctypes.Structure):
                 ("eps", ctypes.c_float), ("chunk_row", ctypes.c_int),
                 ("chunk_col", ctypes.c_int), ("flags", ctypes.c_uint),
                 ("stream", ctypes.c_void_p)]
+
+
+class BlockWeights(ctypes.Structure):
+    """srnl_block_weights: device pointers of the block parameters."""
+    _fields_ = [("ln1_w", ctypes.c_void_p), ("ln1_b", ctypes.c_void_p),
+                ("wq", ctypes.c_void_p), ("dw_w", ctypes.c_void_p), ("dw_b", ctypes.c_void_p),
+                ("ln2_w", ctypes.c_void_p), ("ln2_b", ctypes.c_void_p),
+                ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("ffn_hidden", ctypes.c_int),
+                ("ln_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -70,8 +82,12 @@ def lib() -> ctypes.CDLL:
         L.srnl_fuse_bwd.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp, sz, vp]
         L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
         L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
+        L.srnl_block_workspace_bytes.argtypes = [i, i, i, i, u]
+        L.srnl_block_workspace_bytes.restype = sz
+        L.srnl_block_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params),
+                                     ctypes.POINTER(BlockWeights), vp, sz, vp]
         for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd", "srnl_fuse_bwd",
-                  "srnl_route_gather", "srnl_init_states"):
+                  "srnl_route_gather", "srnl_init_states", "srnl_block_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
                                        ctypes.POINTER(i)]
@@ -234,3 +250,36 @@ def forward(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: 
     return fuse(y, B, H, W, C, route_mask, scales,
                 out_dtype=x.dtype if out_dtype is None else out_dtype,
                 stream=kw.get("stream"))
+
+
+def block_weights(bw: dict, scales: torch.Tensor, ln_eps: float = 1e-5) -> BlockWeights:
+    """srnl_block_weights from a dict of device tensors: ln1_w, ln1_b, dw_w
+    [C,3,3], dw_b, ln2_w, ln2_b, b1, b2 (fp32) and wq [C,C], w1 [F,C], w2
+    [C,F] (bf16). The tensors must outlive the calls that use the struct."""
+    for k in ("wq", "w1", "w2"):
+        if bw[k].dtype != torch.bfloat16:
+            raise ValueError(f"{k} must be bf16")
+    return BlockWeights(_ptr(bw["ln1_w"]), _ptr(bw["ln1_b"]), _ptr(bw["wq"]), _ptr(bw["dw_w"]),
+                        _ptr(bw["dw_b"]), _ptr(bw["ln2_w"]), _ptr(bw["ln2_b"]), _ptr(bw["w1"]),
+                        _ptr(bw["b1"]), _ptr(bw["w2"]), _ptr(bw["b2"]), _ptr(scales),
+                        int(bw["w1"].shape[0]), ln_eps)
+
+
+def block_fwd(x: torch.Tensor, states: torch.Tensor, weights: BlockWeights, heads: int, d: int,
+              route_mask: int = 15, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, *, params: Optional[Params] = None,
+              **kw) -> torch.Tensor:
+    """srnl_block_fwd: one residual block, x [B,H,W,C] -> out [B,H,W,C] in
+    x's dtype. The workspace is allocated here (torch) unless given."""
+    B, H, W, C = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = lib().srnl_block_workspace_bytes(B, H, W, C, route_mask)
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
+    p = params if params is not None else make_params(states, x, **kw)
+    _check(lib().srnl_block_fwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
+                                ctypes.byref(weights), _ptr(workspace),
+                                int(workspace.numel() * workspace.element_size()),
+                                _ptr(out)), "srnl_block_fwd")
+    return out

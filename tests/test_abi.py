@@ -140,3 +140,35 @@ def test_scan_1d_null_params_and_empty_sequence():
     assert L.srnl_scan_1d(None, 1, 4, 8, 2, 4, None, None) == srnl.SRNL_ERR_PTR
     assert _scan_1d(N=0) == srnl.SRNL_OK      # empty sequence: no-op, no pointer needed
     assert _scan_1d(B=0) == srnl.SRNL_OK
+
+
+def _block(B=1, H=2, W=2, C=64, heads=2, d=32, mask=15, q=None, F=128, eps=1e-5,
+           weights=True, params=True):
+    p = srnl.Params(None, q, 0, 0.9, 1e-6, 0, 0, 0, None)
+    w = srnl.BlockWeights(*([None] * 12), F, eps)
+    return srnl.lib().srnl_block_fwd(None, B, H, W, C, heads, d, mask,
+                                     ctypes.byref(p) if params else None,
+                                     ctypes.byref(w) if weights else None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(params=False), srnl.SRNL_ERR_PTR),
+    (dict(weights=False), srnl.SRNL_ERR_PTR),
+    (dict(q=1), srnl.SRNL_ERR_ARG),                   # the block forms its own queries
+    (dict(C=48, heads=3, d=16), srnl.SRNL_ERR_ARG),   # block channels not supported
+    (dict(C=512, heads=16, d=32), srnl.SRNL_ERR_ARG),
+    (dict(F=40), srnl.SRNL_ERR_ARG),                  # hidden width not a multiple of 32
+    (dict(F=0), srnl.SRNL_ERR_ARG),
+    (dict(eps=0.0), srnl.SRNL_ERR_ARG),
+    (dict(C=60, heads=2, d=30), srnl.SRNL_ERR_ARG),   # head dim
+])
+def test_block_argument_errors(kw, status):
+    assert _block(**kw) == status
+    assert srnl.lib().srnl_last_error().decode() != ""
+
+
+def test_block_empty_grid_is_a_no_op():
+    assert _block(B=0) == srnl.SRNL_OK
+    assert srnl.lib().srnl_block_workspace_bytes(0, 2, 2, 64, 15) == 0
+    # u, q, s planes and four route planes, each 64-float aligned
+    assert srnl.lib().srnl_block_workspace_bytes(1, 2, 3, 64, 15) == 4 * (3 * 384 + 4 * 384)
