@@ -332,6 +332,116 @@ def main_stages(args):
     print(json.dumps(rec), flush=True)
 
 
+def block_flops_per_token(C: int, F: int) -> int:
+    """Algorithmic flops of the block around the operator, per token (FMA =
+    2): the query projection 2C^2, the depthwise 3x3 2*9C, the feed-forward
+    network 4CF; the norms, GELU and residual adds are left out."""
+    return 2 * C * C + 18 * C + 4 * C * F
+
+
+def main_block56(args):
+    """One residual block around the operator (srnl_block_fwd) at the
+    hierarchical stage-1 shape: B=64, 56x56, C=64 = 2 heads x d=32, FFN
+    hidden 256, bf16 input (AR(1) rows, seed 2), block parameters seed 2.
+    value = tokens/s of the whole block. The scan and the fusion are then
+    timed again on the block's own u and q (left in its workspace), and the
+    block's two kernels are given the remainder."""
+    import numpy as np
+    import torch
+    from self_referential_memory_amd import srnl, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.hier56()
+    F = 256
+    bw = synth.block_weights(2, wl.C, F)
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    dw = dict(ln1_w=t(bw.ln1_w), ln1_b=t(bw.ln1_b), wq=t(bw.wq, torch.bfloat16), dw_w=t(bw.dw_w),
+              dw_b=t(bw.dw_b), ln2_w=t(bw.ln2_w), ln2_b=t(bw.ln2_b), w1=t(bw.w1, torch.bfloat16),
+              b1=t(bw.b1), w2=t(bw.w2, torch.bfloat16), b2=t(bw.b2))
+    x = t(wl.x, torch.bfloat16)
+    st = t(wl.states)
+    sc = t(wl.scales)
+    w = srnl.block_weights(dw, sc, bw.ln_eps)
+    B, H, W, C = wl.B, wl.H, wl.W, wl.C
+    nbytes = srnl.lib().srnl_block_workspace_bytes(B, H, W, C, 15)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty_like(x)
+    p = srnl.make_params(st, x)
+
+    def step():
+        srnl.block_fwd(x, st, w, wl.heads, wl.d, 15, out=out, workspace=ws, params=p)
+
+    def timed(fn, steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms = timed(step, args.steps)
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    # the operator and the fusion alone, on the block's u and q
+    plane = (B * H * W * C + 63) // 64 * 64
+    u = ws[:B * H * W * C].view(B, H, W, C)
+    q = ws[plane:plane + B * H * W * C].view(B, H, W, C)
+    y = ws[3 * plane:3 * plane + 4 * B * H * W * C].view(4, B, H * W, C)
+    sf = torch.empty((B, H, W, C), dtype=torch.float32, device=dev)
+    pq = srnl.make_params(st, u, q)
+    scan_ms = timed(lambda: srnl.scan_fwd(u, st, wl.heads, wl.d, 15, out=y, params=pq), args.steps)
+    fuse_ms = timed(lambda: srnl.fuse(y, B, H, W, C, 15, sc, out=sf), args.steps)
+    ntok = B * H * W
+    units = ntok * wl.heads
+    srnl_flops = algorithmic_flops_per_unit(wl.d) * units * 4
+    blk_flops = block_flops_per_token(C, F) * ntok
+    achieved = srnl_flops / (scan_ms / 1000.0) / 1e12
+    rest_ms = step_ms - scan_ms - fuse_ms
+    # the block kernels' compulsory bytes: pre reads x, writes u and q; post
+    # reads x, u, s and writes out
+    blk_bytes = ntok * C * (2 + 8 + 2 + 4 + 4 + 2)
+    rec = {
+        "metric": "VisionHOPE block fwd tokens/s (SRNL 4 routes + depthwise branch + FFN)",
+        "value": ntok / (ms / 1000.0), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "block56: one residual block at the hierarchical stage-1 shape, "
+                               "B=64, 56x56, C=64 = 2 heads x d=32, FFN hidden 256, bf16 input, "
+                               "bf16 projection weights, fp32 arithmetic, seed 2",
+                   "B": B, "H": H, "W": W, "C": C, "heads": wl.heads, "d": wl.d, "ffn_hidden": F,
+                   "routes": 4, "input_dtype": "bf16", "parallelism": "single GPU"},
+        "roofline": {"kernel": "scan_kernel (on u with queries q, fp32)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "scan_ms": scan_ms, "algorithmic_flops_per_launch": srnl_flops},
+        "kernels": {
+            "block_step_ms": step_ms, "scan_ms": scan_ms, "fuse_ms": fuse_ms,
+            "block_pre_post_ms": rest_ms,
+            "block_pre_post_algorithmic_bytes": blk_bytes,
+            "block_pre_post_GBs": blk_bytes / (rest_ms / 1000.0) / 1e9 if rest_ms > 0 else None,
+            "block_pre_post_algorithmic_flops": blk_flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import block as OB
+        n = min(args.cpu_items, 8)
+        t0 = time.perf_counter()
+        OB.block_forward(wl.x[:n], wl.states, wl.scales, bw, wl.heads, wl.d)
+        dtc = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": n * H * W / dtc, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch items 0..{n - 1} of {B}, the block oracle (the single-threaded "
+                      f"double-precision operator oracle plus numpy float64), {dtc:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main_hier56_bwd(args):
     """Backward of the hier56 step: srnl_fuse_bwd + srnl_scan_bwd for a given
     dL/d(fused output), forward outputs and inputs resident in HBM."""
@@ -428,11 +538,12 @@ def main():
     ap.add_argument("--pmc-passes", action="store_true",
                     help="print the counter passes, one line each: NAME COUNTER...")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
-    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "stages"),
+    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "stages", "block56"),
                     default="hier56",
                     help="hier56: the 2-D four-route operator (default); seq1d: the "
                          "standalone 1-D SRNL; hier56_bwd: its backward pass; stages: the "
-                         "forward on every stage shape")
+                         "forward on every stage shape; block56: one residual block around "
+                         "the operator at the 56x56 shape")
     args = ap.parse_args()
     if args.pmc_passes:
         for name, counters in PMC_PASSES:
@@ -448,6 +559,9 @@ def main():
         sys.exit(2)
     if args.workload == "seq1d":
         main_seq1d(args)
+        return
+    if args.workload == "block56":
+        main_block56(args)
         return
     if args.workload == "hier56_bwd":
         main_hier56_bwd(args)
