@@ -695,7 +695,10 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
 
 // Per-chain record of the forward that the windowed backward reads (SAVE):
 // every chunk's boundary rows and closing Q_L, and every 16-token window's
-// opening Q_0 and its u_t rows (windows counted from each chunk start).
+// opening Q_0, its u_t rows and its tokens' transition scalars (windows
+// counted from each chunk start). Scalars of a token, 16 floats: 1/sqrt(|k|^2
+// + eps), |k^|^2, |e|^2, g, eta, alpha, 1 - alpha, u = eta g / (1 - alpha),
+// eta', eta'', the branch bits (SCB_*), b_eta . x, b_alpha . x, 3 unused.
 // Chains are chain_floats apart; inside a chain the layout depends on the
 // route's chunk count nch and window slots per chunk nwc.
 struct FwdSave {
@@ -713,8 +716,15 @@ template <int D> struct SaveLayout {
     __host__ __device__ long long o_u(long long c, long long w) const {
         return nch * (BR + D * D) + nch * nwc * D * D + (c * nwc + w) * 16 * D;
     }
-    __host__ __device__ long long floats() const { return nch * (BR + D * D + nwc * (D * D + 16 * D)); }
+    __host__ __device__ long long o_sc(long long c, long long w) const {
+        return nch * (BR + D * D) + nch * nwc * (D * D + 16 * D) + (c * nwc + w) * 256;
+    }
+    __host__ __device__ long long floats() const {
+        return nch * (BR + D * D + nwc * (D * D + 16 * D + 256));
+    }
 };
+// branch bits of a recorded token: soft-cap series, hard cap taken, clamp taken
+constexpr int SCB_SERIES = 1, SCB_HARD = 2, SCB_CLAMP = 4;
 
 template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false>
 __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
@@ -1019,26 +1029,44 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                                                             : alpha_max * sigmoidf(ar);
                 const float g = sqrtf(ne2 * nkh2);
                 const float m = 1.0f - alpha;
-                float eta1 = eta;
+                float eta1 = eta, uu = 0.f;
+                int bits = 0;
                 if (flags & F_NO_CAP) {
                     eta1 = eta;
                 } else if (flags & F_HARD_CAP) {
-                    if (g > 0.0f && m < eta * g)
+                    if (g > 0.0f && m < eta * g) {
                         eta1 = m * __builtin_amdgcn_rcpf(g);
+                        bits |= SCB_HARD;
+                    }
                 } else if (g > 0.0f) {
-                    const float uu = eta * g * __builtin_amdgcn_rcpf(m);
-                    eta1 = (uu < 1e-3f) ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
-                                        : m * tanhf(uu) * __builtin_amdgcn_rcpf(g);
+                    uu = eta * g * __builtin_amdgcn_rcpf(m);
+                    const bool series = uu < 1e-3f;
+                    eta1 = series ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
+                                  : m * tanhf(uu) * __builtin_amdgcn_rcpf(g);
+                    if (series)
+                        bits |= SCB_SERIES;
                 }
                 float eta2 = eta1;
                 if (!(flags & F_NO_CLAMP) && nkh2 > 0.0f) {
                     const float cap = 2.0f * alpha * __builtin_amdgcn_rcpf(nkh2);
-                    if (cap < eta2)
+                    if (cap < eta2) {
                         eta2 = cap;
+                        bits |= SCB_CLAMP;
+                    }
                 }
                 if (ep == 0) {
                     AL[u] = alpha;
                     EH[u] = eta2;
+                }
+                if constexpr (SAVE) {
+                    if (ep == 0) {
+                        float4 *ds = reinterpret_cast<float4 *>(
+                            svc + sl.o_sc(c0 / L, (s0 - c0) / 16 + u / 16) + (u % 16) * 16);
+                        ds[0] = make_float4(inv, nkh2, ne2, g);
+                        ds[1] = make_float4(eta, alpha, m, uu);
+                        ds[2] = make_float4(eta1, eta2, __int_as_float(bits), er);
+                        ds[3] = make_float4(ar, 0.f, 0.f, 0.f);
+                    }
                 }
             } else {
                 // padding token: leaves Q unchanged
