@@ -1262,14 +1262,16 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
                 const float4 nnv = ld4(Nn + win * 16 * NS + lm * NS + 4 * lk);
                 const float wg = WG[win];
+                // K^^T operand of the Q update with diag(R[15]) folded in
+                // (off the window's dependency chain, unlike scaling U)
                 float4 kt[NJ];
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
                     const int jt = jg * NJ + jl;
-                    kt[jl] = make_float4(KHa[ix(tb + 4 * lk, 16 * jt + lm)],
-                                         KHa[ix(tb + 4 * lk + 1, 16 * jt + lm)],
-                                         KHa[ix(tb + 4 * lk + 2, 16 * jt + lm)],
-                                         KHa[ix(tb + 4 * lk + 3, 16 * jt + lm)]);
+                    kt[jl] = make_float4(KHa[ix(tb + 4 * lk, 16 * jt + lm)] * rb.x,
+                                         KHa[ix(tb + 4 * lk + 1, 16 * jt + lm)] * rb.y,
+                                         KHa[ix(tb + 4 * lk + 2, 16 * jt + lm)] * rb.z,
+                                         KHa[ix(tb + 4 * lk + 3, 16 * jt + lm)] * rb.w);
                 }
                 if (JS == 2) {
                     float *xb = XB + ((win & 1) * NTC + it) * 512 + 4 * lane;
@@ -1308,10 +1310,6 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     Z = mfma4(nnv.z, U[2], Z);
                     Z = mfma4(nnv.w, U[3], Z);
                 }
-                U[0] *= rb.x;
-                U[1] *= rb.y;
-                U[2] *= rb.z;
-                U[3] *= rb.w;
 #pragma unroll
                 for (int jl = 0; jl < NJ; ++jl) {
                     qacc[jl] *= wg;
