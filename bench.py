@@ -77,7 +77,14 @@ def algorithmic_bytes(wl, R: int) -> dict:
 
 
 def src_sha() -> str:
-    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+    """sha256 prefix of the library's kernel sources: every file of csrc/ in
+    name order, concatenated."""
+    d = os.path.dirname(SRC)
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".inc")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_counters():
