@@ -1,7 +1,9 @@
 /*
  * srnl.h -- C ABI of libsrnl.so: the forward pass of the stabilised SRNL
  * operator over a 2-D feature grid (four routes, row/column-aligned chunks,
- * learned channel-scale fusion) on AMD Instinct MI355X (gfx950).
+ * learned channel-scale fusion) on AMD Instinct MI355X (gfx950), with its
+ * backward pass, the standalone 1-D operator and one residual block around
+ * the operator.
  *
  * Sources, cited by page title and section:
  *   [README]   "VisionHOPE" README (github.com/PSRben/VisionHOPE), sections
@@ -182,9 +184,14 @@ srnl_status srnl_fuse(const float *y_routes, int B, int H, int W, int C,
  *   dstates [4][heads][3d^2+2d] fp32 = dL/d(initial states), summed over
  *           the batch (overwritten; zero for inactive routes).
  *   dy      [R][B][H*W][C] fp32 in the layout srnl_scan_fwd writes.
- * Per chain it re-runs the forward to record the boundary of every chunk,
- * then walks the chunks backwards, re-running each chunk to record the
- * working state after every token, and walks the tokens backwards.
+ * At d = 32 with the readout after the write, a recording forward writes,
+ * per chain, every chunk's boundary and closing state and every 16-token
+ * window's opening state, update rows and transition scalars into the
+ * workspace; the adjoint then walks the chunks and windows backwards, 16
+ * tokens at a time. Otherwise each chain re-runs the forward to record the
+ * boundary of every chunk, then walks the chunks backwards, re-running each
+ * chunk to record the working state after every token, and walks the tokens
+ * backwards. Sums run in a fixed order (bitwise reproducible).
  * The workspace is caller-owned device memory of at least
  * srnl_scan_bwd_workspace_bytes(...) bytes; its contents are scratch.
  * Errors: as srnl_scan_fwd, plus SRNL_ERR_WORKSPACE, and SRNL_ERR_PTR for
