@@ -1911,7 +1911,7 @@ srnl_status dispatch_scan_bwd(int d, const void *x, const srnl_params *p, int B,
     return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
 }
 
-constexpr long long kFuseBwdRows = 2048;   // rows per partial-sum block of srnl_fuse_bwd
+constexpr long long kFuseBwdRows = 256;    // grid cells per partial-sum block of srnl_fuse_bwd
 
 long long fuse_bwd_blocks(int B, int H, int W)
 {
@@ -2150,12 +2150,12 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be device memory");
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *part = static_cast<float *>(workspace);
-    hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk), R), dim3(256), 0, st, dout, y,
+    hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, dout, y,
                        scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
     s = launch_check("fuse_bwd_kernel");
     if (s != SRNL_OK)
         return s;
-    hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C, 256)), dim3(256), 0, st, part,
+    hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C * 64, 256)), dim3(256), 0, st, part,
                        dscales, C, route_mask, static_cast<int>(nblk));
     return launch_check("fuse_bwd_scales_kernel");
 }
