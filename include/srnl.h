@@ -30,6 +30,9 @@
  *   - Errors are returned as srnl_status; nothing throws across the ABI.
  *     srnl_last_error() gives a thread-local human-readable detail.
  *   - Empty grids (B, H or W equal to 0) are valid and launch nothing.
+ *   - Tensor pointers must be 16-byte aligned (the kernels move 16-byte
+ *     vectors); a misaligned one is SRNL_ERR_PTR. srnl_route_gather is the
+ *     exception: it accepts any element-aligned view.
  */
 #ifndef SRNL_H
 #define SRNL_H

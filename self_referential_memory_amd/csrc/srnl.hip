@@ -2037,6 +2037,8 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_PTR, "x, out and states must be device memory");
     if (p->q && !is_device_ptr(p->q))
         return fail(SRNL_ERR_PTR, "q must be device memory");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(p->states) || (p->q && !aligned16(p->q)))
+        return fail(SRNL_ERR_PTR, "x, q, out and states must be 16-byte aligned");
     if (p->in_dtype == SRNL_F32)
         return dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out);
     return dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
@@ -2069,6 +2071,8 @@ srnl_status srnl_fuse(const float *y, int B, int H, int W, int C, unsigned route
         return SRNL_OK;
     if (!is_device_ptr(y) || !is_device_ptr(scales) || !is_device_ptr(out))
         return fail(SRNL_ERR_PTR, "y_routes, scales and out must be device memory");
+    if (!aligned16(y) || !aligned16(scales) || !aligned16(out))
+        return fail(SRNL_ERR_PTR, "y_routes, scales and out must be 16-byte aligned");
     const PlaneShape ps = plane_shape(C / 4);
     const dim3 grid((H * W + ps.ty - 1) / ps.ty, B < 65535 ? B : 65535), block(ps.cv, ps.ty);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -2110,6 +2114,9 @@ srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_PTR, "x, states, dy, dx, dstates and workspace must be device memory");
     if (p->q && (!is_device_ptr(p->q) || !is_device_ptr(dq)))
         return fail(SRNL_ERR_PTR, "with separate queries, q and dq must be device memory");
+    if (!aligned16(x) || !aligned16(p->states) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dstates) || !aligned16(workspace) || (p->q && (!aligned16(p->q) || !aligned16(dq))))
+        return fail(SRNL_ERR_PTR, "x, q, states, dy, dx, dq, dstates and workspace must be 16-byte aligned");
     if (l.chains > INT_MAX)
         return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
     float *ws = static_cast<float *>(workspace);
@@ -2148,6 +2155,9 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W
     if (!is_device_ptr(dout) || !is_device_ptr(y) || !is_device_ptr(scales) ||
         !is_device_ptr(dyr) || !is_device_ptr(dscales) || !is_device_ptr(workspace))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be device memory");
+    if (!aligned16(dout) || !aligned16(y) || !aligned16(scales) || !aligned16(dyr) ||
+        !aligned16(dscales) || !aligned16(workspace))
+        return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *part = static_cast<float *>(workspace);
     hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, dout, y,

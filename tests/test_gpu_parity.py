@@ -467,3 +467,36 @@ def test_scan_1d_query_dtype_must_match():
 
 def srnl_state(d):
     return 3 * d * d + 2 * d
+
+
+def test_misaligned_tensors_are_pointer_errors():
+    """Every entry point but the gather moves 16-byte vectors and rejects a
+    tensor that starts off a 16-byte boundary, before launching anything."""
+    wl = synth.make("mis", 1, 4, 4, 64, 2, 32, "f32", 51)
+    B, H, W, C = wl.B, wl.H, wl.W, wl.C
+    n = B * H * W * C
+    base = torch.zeros(n + 4, dtype=torch.float32, device=DEV)
+    good = torch.from_numpy(wl.x).to(DEV)
+    bad = base[1:1 + n].view(B, H, W, C)            # 4 bytes past an aligned address
+    bad.copy_(good)
+    st = torch.from_numpy(wl.states).to(DEV)
+    sc = torch.from_numpy(wl.scales).to(DEV)
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd(bad, st, wl.heads, wl.d, 15)
+    assert e.value.status == srnl.SRNL_ERR_PTR
+    y = srnl.scan_fwd(good, st, wl.heads, wl.d, 15)
+    ybase = torch.zeros(y.numel() + 4, dtype=torch.float32, device=DEV)
+    ybad = ybase[1:1 + y.numel()].view(y.shape)
+    ybad.copy_(y)
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.fuse(ybad, B, H, W, C, 15, sc)
+    assert e.value.status == srnl.SRNL_ERR_PTR
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_bwd(good, st, wl.heads, wl.d, ybad, 15)
+    assert e.value.status == srnl.SRNL_ERR_PTR
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.fuse_bwd(bad, y, B, H, W, C, 15, sc)
+    assert e.value.status == srnl.SRNL_ERR_PTR
+    # the aligned calls still work
+    srnl.fuse(y, B, H, W, C, 15, sc)
+    torch.cuda.synchronize()
