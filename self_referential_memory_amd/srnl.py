@@ -256,13 +256,24 @@ def block_weights(bw: dict, scales: torch.Tensor, ln_eps: float = 1e-5) -> Block
     """srnl_block_weights from a dict of device tensors: ln1_w, ln1_b, dw_w
     [C,3,3], dw_b, ln2_w, ln2_b, b1, b2 (fp32) and wq [C,C], w1 [F,C], w2
     [C,F] (bf16). The tensors must outlive the calls that use the struct."""
-    for k in ("wq", "w1", "w2"):
-        if bw[k].dtype != torch.bfloat16:
-            raise ValueError(f"{k} must be bf16")
-    return BlockWeights(_ptr(bw["ln1_w"]), _ptr(bw["ln1_b"]), _ptr(bw["wq"]), _ptr(bw["dw_w"]),
-                        _ptr(bw["dw_b"]), _ptr(bw["ln2_w"]), _ptr(bw["ln2_b"]), _ptr(bw["w1"]),
-                        _ptr(bw["b1"]), _ptr(bw["w2"]), _ptr(bw["b2"]), _ptr(scales),
-                        int(bw["w1"].shape[0]), ln_eps)
+    # the library sees only pointers: every shape is checked here
+    C = int(bw["wq"].shape[0])
+    F = int(bw["w1"].shape[0])
+    shapes = {"ln1_w": (C,), "ln1_b": (C,), "wq": (C, C), "dw_w": (C, 3, 3), "dw_b": (C,),
+              "ln2_w": (C,), "ln2_b": (C,), "w1": (F, C), "b1": (F,), "w2": (C, F), "b2": (C,)}
+    for k, shp in shapes.items():
+        if tuple(bw[k].shape) != shp:
+            raise ValueError(f"{k} has shape {tuple(bw[k].shape)}, expected {shp}")
+        want = torch.bfloat16 if k in ("wq", "w1", "w2") else torch.float32
+        if bw[k].dtype != want:
+            raise ValueError(f"{k} must be {want}")
+    if tuple(scales.shape) != (4, C) or scales.dtype != torch.float32:
+        raise ValueError(f"scales must be float32 of shape (4, {C})")
+    w = BlockWeights(_ptr(bw["ln1_w"]), _ptr(bw["ln1_b"]), _ptr(bw["wq"]), _ptr(bw["dw_w"]),
+                     _ptr(bw["dw_b"]), _ptr(bw["ln2_w"]), _ptr(bw["ln2_b"]), _ptr(bw["w1"]),
+                     _ptr(bw["b1"]), _ptr(bw["w2"]), _ptr(bw["b2"]), _ptr(scales), F, ln_eps)
+    w.channels = C
+    return w
 
 
 def block_fwd(x: torch.Tensor, states: torch.Tensor, weights: BlockWeights, heads: int, d: int,
@@ -272,9 +283,13 @@ def block_fwd(x: torch.Tensor, states: torch.Tensor, weights: BlockWeights, head
     """srnl_block_fwd: one residual block, x [B,H,W,C] -> out [B,H,W,C] in
     x's dtype. The workspace is allocated here (torch) unless given."""
     B, H, W, C = x.shape
+    if getattr(weights, "channels", C) != C:
+        raise ValueError(f"weights are for C = {weights.channels}, x has C = {C}")
     if out is None:
         out = torch.empty_like(x)
     nbytes = lib().srnl_block_workspace_bytes(B, H, W, C, route_mask)
+    if workspace is not None and workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace smaller than srnl_block_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
     p = params if params is not None else make_params(states, x, **kw)

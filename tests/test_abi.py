@@ -172,3 +172,25 @@ def test_block_empty_grid_is_a_no_op():
     assert srnl.lib().srnl_block_workspace_bytes(0, 2, 2, 64, 15) == 0
     # u, q, s planes and four route planes, each 64-float aligned
     assert srnl.lib().srnl_block_workspace_bytes(1, 2, 3, 64, 15) == 4 * (3 * 384 + 4 * 384)
+
+
+def test_block_weights_binding_checks_shapes():
+    """The library sees only pointers, so the binding checks every block
+    parameter's shape and dtype (on CPU tensors: nothing is launched)."""
+    import torch
+    C, F = 64, 128
+    f, b = torch.float32, torch.bfloat16
+    bw = dict(ln1_w=torch.ones(C, dtype=f), ln1_b=torch.zeros(C, dtype=f),
+              wq=torch.zeros(C, C, dtype=b), dw_w=torch.zeros(C, 3, 3, dtype=f),
+              dw_b=torch.zeros(C, dtype=f), ln2_w=torch.ones(C, dtype=f),
+              ln2_b=torch.zeros(C, dtype=f), w1=torch.zeros(F, C, dtype=b),
+              b1=torch.zeros(F, dtype=f), w2=torch.zeros(C, F, dtype=b), b2=torch.zeros(C, dtype=f))
+    sc = torch.ones(4, C, dtype=f)
+    w = srnl.block_weights(bw, sc)
+    assert w.ffn_hidden == F and w.channels == C
+    for k, bad in (("w2", torch.zeros(C, F + 32, dtype=b)), ("w1", torch.zeros(F, C, dtype=f)),
+                   ("dw_w", torch.zeros(C, 9, dtype=f)), ("b1", torch.zeros(F + 1, dtype=f))):
+        with pytest.raises(ValueError):
+            srnl.block_weights(dict(bw, **{k: bad}), sc)
+    with pytest.raises(ValueError):
+        srnl.block_weights(bw, torch.ones(4, C + 4, dtype=f))

@@ -126,7 +126,7 @@ def test_block_rejects_separate_queries_and_misaligned_weights():
         srnl.block_fwd(x, st, w, 2, 32, 15, params=srnl.make_params(st, x, x.clone()))
     assert e.value.status == srnl.SRNL_ERR_ARG
     big = torch.zeros(64 * 64 + 8, dtype=torch.bfloat16, device=DEV)
-    dw["wq"] = big[4:4 + 64 * 64]                     # 8-byte offset
+    dw["wq"] = big[4:4 + 64 * 64].view(64, 64)        # 8-byte offset
     w = srnl.block_weights(dw, sc)
     with pytest.raises(srnl.SrnlError) as e:
         srnl.block_fwd(x, st, w, 2, 32, 15)
