@@ -115,6 +115,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(t: Optional[torch.Tensor], shape, dtype, name: str) -> None:
+    """The library sees only pointers: buffer shapes and dtypes are checked here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _state_shape(heads: int, d: int):
+    return (4, heads, 3 * d * d + 2 * d)
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -156,8 +170,10 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
     """srnl_scan_fwd: x [B,H,W,C] -> per-route outputs [R,B,H*W,C] fp32."""
     B, H, W, C = x.shape
     R = bin(route_mask & 15).count("1")
+    _expect(states, _state_shape(heads, d), torch.float32, "states")
     if out is None:
         out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
+    _expect(out, (R, B, H * W, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, **kw)
     _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
                                ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
@@ -169,8 +185,10 @@ def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
             chunk: int = 0, params: Optional[Params] = None, **kw) -> torch.Tensor:
     """srnl_scan_1d: x [B,N,C] -> y [B,N,C] fp32 (chunk 0 selects 64 tokens)."""
     B, N, C = x.shape
+    _expect(states, (heads, 3 * d * d + 2 * d), torch.float32, "states")
     if out is None:
         out = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
+    _expect(out, (B, N, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, chunk_row=chunk, **kw)
     _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
            "srnl_scan_1d")
@@ -181,6 +199,9 @@ def fuse(y: torch.Tensor, B: int, H: int, W: int, C: int, route_mask: int,
          scales: torch.Tensor, out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
          stream=None) -> torch.Tensor:
     """srnl_fuse: per-route outputs -> restored, channel-scaled sum [B,H,W,C]."""
+    R = bin(route_mask & 15).count("1")
+    _expect(y, (R, B, H * W, C), torch.float32, "y")
+    _expect(scales, (4, C), torch.float32, "scales")
     if out is None:
         out = torch.empty((B, H, W, C), dtype=out_dtype, device=y.device)
     _check(lib().srnl_fuse(_ptr(y), B, H, W, C, route_mask, _ptr(scales),
@@ -194,6 +215,9 @@ def scan_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torc
     """srnl_scan_bwd: dy [R,B,H*W,C] fp32 -> (dx [B,H,W,C], dq or None, dstates
     [4,heads,3d^2+2d]), all fp32. The workspace is allocated here (torch)."""
     B, H, W, C = x.shape
+    R = bin(route_mask & 15).count("1")
+    _expect(states, _state_shape(heads, d), torch.float32, "states")
+    _expect(dy, (R, B, H * W, C), torch.float32, "dy")
     p = params if params is not None else make_params(states, x, q, **kw)
     nbytes = lib().srnl_scan_bwd_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
@@ -209,6 +233,10 @@ def scan_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torc
 def fuse_bwd(dout: torch.Tensor, y: torch.Tensor, B: int, H: int, W: int, C: int,
              route_mask: int, scales: torch.Tensor, stream=None):
     """srnl_fuse_bwd: dout [B,H,W,C] fp32 -> (dy_routes [R,B,H*W,C], dscales [4,C])."""
+    R = bin(route_mask & 15).count("1")
+    _expect(dout, (B, H, W, C), torch.float32, "dout")
+    _expect(y, (R, B, H * W, C), torch.float32, "y")
+    _expect(scales, (4, C), torch.float32, "scales")
     nbytes = lib().srnl_fuse_bwd_workspace_bytes(B, H, W, C, route_mask)
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dout.device)
     dyr = torch.empty_like(y)
@@ -285,8 +313,10 @@ def block_fwd(x: torch.Tensor, states: torch.Tensor, weights: BlockWeights, head
     B, H, W, C = x.shape
     if getattr(weights, "channels", C) != C:
         raise ValueError(f"weights are for C = {weights.channels}, x has C = {C}")
+    _expect(states, _state_shape(heads, d), torch.float32, "states")
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, x.shape, x.dtype, "out")
     nbytes = lib().srnl_block_workspace_bytes(B, H, W, C, route_mask)
     if workspace is not None and workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace smaller than srnl_block_workspace_bytes")

@@ -194,3 +194,24 @@ def test_block_weights_binding_checks_shapes():
             srnl.block_weights(dict(bw, **{k: bad}), sc)
     with pytest.raises(ValueError):
         srnl.block_weights(bw, torch.ones(4, C + 4, dtype=f))
+
+
+def test_binding_checks_buffer_shapes():
+    """The binding rejects mis-shaped states, outputs and gradients before
+    calling the library (CPU tensors: the checks come first)."""
+    import torch
+    x = torch.zeros(1, 4, 4, 64)
+    st = torch.zeros(4, 2, 3 * 32 * 32 + 2 * 32)
+    with pytest.raises(ValueError):
+        srnl.scan_fwd(x, st[:, :1], 2, 32, 15)              # one head's states for two heads
+    with pytest.raises(ValueError):
+        srnl.scan_fwd(x, st, 2, 32, 15, out=torch.zeros(3, 1, 16, 64))
+    with pytest.raises(ValueError):
+        srnl.fuse(torch.zeros(4, 1, 16, 64), 1, 4, 4, 64, 15, torch.zeros(4, 32))
+    with pytest.raises(ValueError):
+        srnl.scan_bwd(x, st, 2, 32, torch.zeros(2, 1, 16, 64), 15)
+    with pytest.raises(ValueError):
+        srnl.fuse_bwd(torch.zeros(1, 4, 4, 32), torch.zeros(4, 1, 16, 64), 1, 4, 4, 64, 15,
+                      torch.zeros(4, 64))
+    with pytest.raises(ValueError):
+        srnl.scan_1d(torch.zeros(1, 10, 64), st, 2, 32)     # 1-D states are [heads][...]
