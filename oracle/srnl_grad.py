@@ -2,11 +2,10 @@
 
 A plain float64 PyTorch (CPU) restatement of the operator in its five-memory
 form, differentiated by autograd. Only the test suite and the smoke check
-may use it. It shares
-no code with the HIP library, and none with the C oracle either: it is a
-second, independent reading of the same passages, so that the C oracle pins
-its forward values and central finite differences of the C oracle pin its
-gradients.
+may use it. It shares no code with the HIP library, and none with the C
+oracle either: it is a second, independent reading of the same passages, so
+that the C oracle pins its forward values and central finite differences of
+the C oracle pin its gradients.
 
 Sources, cited by page title and section:
   [README]   "VisionHOPE" README: "SRNL and VisionHOPE operator" (training
