@@ -50,7 +50,8 @@ typedef enum {
     SRNL_ERR_DTYPE = -2,     /* unknown dtype */
     SRNL_ERR_PTR = -3,       /* NULL, or not device memory where required */
     SRNL_ERR_WORKSPACE = -4, /* workspace missing or smaller than required */
-    SRNL_ERR_HIP = -5        /* a HIP runtime call or launch failed */
+    SRNL_ERR_HIP = -5,       /* a HIP runtime call or launch failed */
+    SRNL_ERR_NONFINITE = -6  /* SRNL_FLAG_CHECK_FINITE found NaN or Inf (outputs are written) */
 } srnl_status;
 
 typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
@@ -76,6 +77,11 @@ typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
 #define SRNL_FLAG_READ_BEFORE  0x10u /* y_t read before token t's write */
 #define SRNL_FLAG_FREEZE_KV    0x20u /* only M_c is written; M_k, M_v, m_eta, m_alpha keep
                                         their initial values (frozen key/value and dynamics) */
+/* Count NaN and Inf in x, q and the outputs of srnl_scan_fwd / srnl_scan_1d
+ * and report them through the status (SRNL_ERR_NONFINITE). The count needs
+ * a workspace of srnl_scan_workspace_bytes, and the call then waits for its
+ * stream to finish. Other entry points ignore the flag. */
+#define SRNL_FLAG_CHECK_FINITE 0x40u
 
 /* Floats of initial state per (route, head): 3d^2 + 2d. */
 #define SRNL_STATE_FLOATS(d) (3 * (d) * (d) + 2 * (d))
@@ -98,6 +104,11 @@ typedef struct {
     int chunk_col;        /* 0: chunk = H on column routes; > 0: that length */
     unsigned flags;       /* SRNL_FLAG_* */
     void *stream;         /* hipStream_t */
+    /* Device workspace for srnl_scan_fwd / srnl_scan_1d, at least
+     * srnl_scan_workspace_bytes(...) bytes (that is 0, and this may be NULL,
+     * unless SRNL_FLAG_CHECK_FINITE is set); caller-owned, contents scratch. */
+    void *workspace;
+    size_t workspace_bytes;
 } srnl_params;
 
 /*
@@ -133,6 +144,15 @@ typedef struct {
 srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
                           int d, unsigned route_mask, const srnl_params *params,
                           float *out);
+
+/*
+ * srnl_scan_workspace_bytes -- device workspace srnl_scan_fwd needs for these
+ * sizes and params: 0 unless params->flags has SRNL_FLAG_CHECK_FINITE (then
+ * room for two counters, non-finite input and output values). 0 for an
+ * empty grid or invalid arguments.
+ */
+size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                 unsigned route_mask, const srnl_params *params);
 
 /*
  * srnl_scan_1d -- standalone 1-D SRNL [README SRNL and VisionHOPE operator]:

@@ -152,7 +152,7 @@ template <int D> struct ScanCfg {
 
 enum : unsigned {
     F_HARD_CAP = 0x1u, F_NO_CAP = 0x2u, F_NO_CLAMP = 0x4u, F_FIXED_ALPHA = 0x8u,
-    F_READ_BEFORE = 0x10u, F_FREEZE_KV = 0x20u
+    F_READ_BEFORE = 0x10u, F_FREEZE_KV = 0x20u, F_CHECK_FINITE = 0x40u
 };
 
 template <int D, typename InT>
@@ -1449,6 +1449,40 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     }
 }
 
+// ------------------------------------------------------------ finite check
+
+// NaN or Inf: the exponent field is all ones
+__device__ __forceinline__ unsigned nonfinite(float v) { return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u; }
+__device__ __forceinline__ unsigned nonfinite(uint16_t v) { return (v & 0x7F80u) == 0x7F80u; }
+
+// counters[0..1] = 0 (a kernel rather than a memset, so the call can be captured)
+__global__ void zero_counters_kernel(unsigned *__restrict__ counters)
+{
+    if (threadIdx.x < 2)
+        counters[threadIdx.x] = 0u;
+}
+
+// *counter += number of NaN or Inf among v[0 .. n)
+template <typename T>
+__global__ __launch_bounds__(256) void nonfinite_kernel(const T *__restrict__ v, long long n,
+                                                        unsigned *__restrict__ counter)
+{
+    __shared__ unsigned part[4];
+    unsigned c = 0;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<long long>(gridDim.x) * 256)
+        c += nonfinite(v[i]);
+    for (int off = 32; off > 0; off >>= 1)
+        c += __shfl_xor(c, off);
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned t = part[0] + part[1] + part[2] + part[3];
+        if (t)
+            atomicAdd(counter, t);
+    }
+}
+
 // ------------------------------------------------------------ fuse kernel
 
 __device__ __forceinline__ void store4(float *o, float4 a) { *reinterpret_cast<float4 *>(o) = a; }
@@ -1938,7 +1972,7 @@ srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsign
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x3Fu)
+    if (p->flags & ~0x7Fu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
@@ -1966,6 +2000,9 @@ BlockLayout block_layout(int B, int H, int W, int C, unsigned mask)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// workspace of srnl_scan_fwd with SRNL_FLAG_CHECK_FINITE: two counters
+constexpr size_t kScanCheckBytes = 256;
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI
@@ -1981,6 +2018,7 @@ const char *srnl_status_string(srnl_status s)
     case SRNL_ERR_PTR: return "invalid pointer";
     case SRNL_ERR_WORKSPACE: return "workspace too small";
     case SRNL_ERR_HIP: return "HIP error";
+    case SRNL_ERR_NONFINITE: return "non-finite values";
     }
     return "unknown status";
 }
@@ -2027,7 +2065,7 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x3Fu)
+    if (p->flags & ~0x7Fu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
@@ -2039,9 +2077,64 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_PTR, "q must be device memory");
     if (!aligned16(x) || !aligned16(out) || !aligned16(p->states) || (p->q && !aligned16(p->q)))
         return fail(SRNL_ERR_PTR, "x, q, out and states must be 16-byte aligned");
-    if (p->in_dtype == SRNL_F32)
-        return dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out);
-    return dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
+    const bool check = (p->flags & F_CHECK_FINITE) != 0;
+    unsigned *counters = static_cast<unsigned *>(p->workspace);
+    if (check) {
+        if (!counters || p->workspace_bytes < kScanCheckBytes)
+            return fail(SRNL_ERR_WORKSPACE, "SRNL_FLAG_CHECK_FINITE needs srnl_scan_workspace_bytes of workspace");
+        if (!is_device_ptr(counters))
+            return fail(SRNL_ERR_PTR, "workspace must be device memory");
+    }
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    const long long nx = static_cast<long long>(B) * H * W * C;
+    if (check) {
+        hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, st, counters);
+        if (p->in_dtype == SRNL_F32) {
+            hipLaunchKernelGGL(nonfinite_kernel<float>, dim3(grid_for(nx, 256)), dim3(256), 0, st,
+                               static_cast<const float *>(x), nx, counters);
+            if (p->q)
+                hipLaunchKernelGGL(nonfinite_kernel<float>, dim3(grid_for(nx, 256)), dim3(256), 0, st,
+                                   static_cast<const float *>(p->q), nx, counters);
+        } else {
+            hipLaunchKernelGGL(nonfinite_kernel<uint16_t>, dim3(grid_for(nx, 256)), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(x), nx, counters);
+            if (p->q)
+                hipLaunchKernelGGL(nonfinite_kernel<uint16_t>, dim3(grid_for(nx, 256)), dim3(256), 0,
+                                   st, static_cast<const uint16_t *>(p->q), nx, counters);
+        }
+        s = launch_check("nonfinite_kernel (inputs)");
+        if (s != SRNL_OK)
+            return s;
+    }
+    s = (p->in_dtype == SRNL_F32)
+            ? dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out)
+            : dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
+    if (s != SRNL_OK || !check)
+        return s;
+    hipLaunchKernelGGL(nonfinite_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, out, n,
+                       counters + 1);
+    s = launch_check("nonfinite_kernel (outputs)");
+    if (s != SRNL_OK)
+        return s;
+    unsigned host[2] = {0u, 0u};
+    if (hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return fail(SRNL_ERR_HIP, std::string("reading the finite-check counters: ") +
+                                      hipGetErrorString(hipGetLastError()));
+    if (host[0] || host[1])
+        return fail(SRNL_ERR_NONFINITE, std::to_string(host[0]) + " non-finite input values, " +
+                                            std::to_string(host[1]) + " non-finite outputs");
+    return SRNL_OK;
+}
+
+size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                 unsigned route_mask, const srnl_params *p)
+{
+    long long n = 0;
+    if (!p || !valid_d(d) || heads < 1 || C != heads * d ||
+        check_grid(B, H, W, C, route_mask, &n) != SRNL_OK || n == 0)
+        return 0;
+    return (p->flags & F_CHECK_FINITE) ? kScanCheckBytes : 0;
 }
 
 srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,

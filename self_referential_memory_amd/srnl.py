@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsrnl.so"
 
 SRNL_OK, SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE, SRNL_ERR_HIP = (
     0, -1, -2, -3, -4, -5)
+SRNL_ERR_NONFINITE = -6
 SRNL_F32, SRNL_BF16 = 0, 1
 FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = (
     0x1, 0x2, 0x4, 0x8, 0x10)
 FLAG_FREEZE_KV = 0x20
+FLAG_CHECK_FINITE = 0x40
 
-EXPORTS = ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
+EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
            "srnl_route_gather", "srnl_init_states", "srnl_block_fwd",
            "srnl_block_workspace_bytes",
@@ -42,7 +44,8 @@ class Params(ctypes.Structure):
                 ("in_dtype", ctypes.c_int), ("alpha_max", ctypes.c_float),
                 ("eps", ctypes.c_float), ("chunk_row", ctypes.c_int),
                 ("chunk_col", ctypes.c_int), ("flags", ctypes.c_uint),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -73,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.srnl_scan_1d.argtypes = [vp, i, i, i, i, i, ctypes.POINTER(Params), vp]
         L.srnl_fuse.argtypes = [vp, i, i, i, i, u, vp, i, vp, vp]
         sz = ctypes.c_size_t
+        L.srnl_scan_workspace_bytes.argtypes = [i, i, i, i, i, i, u, ctypes.POINTER(Params)]
+        L.srnl_scan_workspace_bytes.restype = sz
         L.srnl_scan_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, u, ctypes.POINTER(Params)]
         L.srnl_scan_bwd_workspace_bytes.restype = sz
         L.srnl_scan_bwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp, vp, sz,
@@ -175,8 +180,20 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
     _expect(out, (R, B, H * W, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, **kw)
-    _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
-                               ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
+    ws = None
+    if p.flags & FLAG_CHECK_FINITE and not p.workspace:
+        # the call waits for the stream when checking, so the buffer outlives its use
+        nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask,
+                                                 ctypes.byref(p))
+        if nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+            p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
+    try:
+        _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
+                                   ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
+    finally:
+        if ws is not None:
+            p.workspace, p.workspace_bytes = None, 0
     return out
 
 
@@ -278,6 +295,42 @@ def forward(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: 
     return fuse(y, B, H, W, C, route_mask, scales,
                 out_dtype=x.dtype if out_dtype is None else out_dtype,
                 stream=kw.get("stream"))
+
+
+class Operator(torch.autograd.Function):
+    """The operator (scan + fuse) as an autograd node: the forward pass is
+    srnl_scan_fwd and srnl_fuse, the backward pass srnl_fuse_bwd and
+    srnl_scan_bwd. Gradients flow to x, the initial states, the scales and
+    the separate queries. The route outputs are kept for the fusion backward;
+    srnl_scan_bwd recomputes everything else from x and the states."""
+
+    @staticmethod
+    def forward(ctx, x, states, scales, q, heads, d, route_mask, kw):
+        B, H, W, C = x.shape
+        y = scan_fwd(x, states, heads, d, route_mask, q, **kw)
+        out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype)
+        ctx.save_for_backward(x, states, scales, q, y)
+        ctx.cfg = (heads, d, route_mask, kw)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, states, scales, q, y = ctx.saved_tensors
+        heads, d, route_mask, kw = ctx.cfg
+        B, H, W, C = x.shape
+        dout = dout.to(torch.float32).contiguous()
+        dyr, dsc = fuse_bwd(dout, y, B, H, W, C, route_mask, scales)
+        dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, **kw)
+        return (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype),
+                None, None, None, None)
+
+
+def operator(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: int, d: int,
+             route_mask: int = 15, q: Optional[torch.Tensor] = None, **kw) -> torch.Tensor:
+    """Differentiable scan + fuse on an NHWC grid; the output has x's dtype.
+    ``kw`` are the srnl_params fields (alpha_max, eps, chunk_row, chunk_col,
+    flags)."""
+    return Operator.apply(x, states, scales, q, heads, d, route_mask, kw)
 
 
 def block_weights(bw: dict, scales: torch.Tensor, ln_eps: float = 1e-5) -> BlockWeights:

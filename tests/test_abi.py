@@ -76,7 +76,7 @@ def _scan(x=0, B=1, H=2, W=2, C=8, heads=2, d=4, mask=15, **kw):
     (dict(eps=float("inf")), srnl.SRNL_ERR_ARG),
     (dict(chunk_row=-1), srnl.SRNL_ERR_ARG),
     (dict(flags=0x100), srnl.SRNL_ERR_ARG),
-    (dict(flags=0x40), srnl.SRNL_ERR_ARG),          # first bit above the known flags
+    (dict(flags=0x80), srnl.SRNL_ERR_ARG),          # first bit above the known flags
     (dict(in_dtype=7), srnl.SRNL_ERR_DTYPE),
     (dict(B=1 << 30, H=1 << 15, W=1 << 15, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # overflow
     (dict(B=1, H=1 << 16, W=1 << 16, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # H*W > INT_MAX
@@ -112,8 +112,24 @@ def test_fuse_and_gather_argument_errors():
 
 def test_status_strings():
     L = srnl.lib()
-    for s in (0, -1, -2, -3, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.srnl_status_string(s).decode() not in ("", "unknown status")
+
+
+def test_scan_workspace_bytes():
+    L = srnl.lib()
+
+    def ws(flags, B=2, H=3, W=4, C=8, heads=2, d=4, mask=15):
+        p = srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, flags, None)
+        return L.srnl_scan_workspace_bytes(B, H, W, C, heads, d, mask, ctypes.byref(p))
+
+    assert ws(0) == 0                               # no check: no workspace
+    assert ws(srnl.FLAG_CHECK_FINITE) >= 8          # two 32-bit counters
+    assert ws(srnl.FLAG_CHECK_FINITE, B=0) == 0     # empty grid
+    assert ws(srnl.FLAG_CHECK_FINITE, C=12) == 0    # invalid shape
+    assert L.srnl_scan_workspace_bytes(1, 2, 2, 8, 2, 4, 15, None) == 0
+    # an empty grid is a no-op with the check as without it
+    assert _scan(B=0, flags=srnl.FLAG_CHECK_FINITE) == srnl.SRNL_OK
 
 
 def _scan_1d(x=0, B=1, N=4, C=8, heads=2, d=4, **kw):

@@ -175,3 +175,48 @@ def test_grad_hier56_full_map():
     """The benchmark's map at full size (56x56, C=64, 2 heads x d=32, four
     routes, AR(1) rows, bf16 input) on two batch items."""
     run_case(synth.make("hier56_b2", 2, 56, 56, 64, 2, 32, "bf16", 2, x_kind="ar1"))
+
+
+@pytest.mark.parametrize("dtype,separate_q", [("f32", False), ("bf16", True)])
+def test_autograd_operator(dtype, separate_q):
+    """srnl.operator under torch.autograd: the forward equals srnl.forward
+    bitwise, and the gradients of x, q, the states and the scales equal the
+    oracle's for the same output gradient (bf16 gradients of bf16 inputs to
+    one bf16 rounding plus the fp32 bar)."""
+    wl = _wl("gauto", 2, 5, 6, 2, 32, dtype=dtype, seed=9, separate_q=separate_q)
+    print(f"[gpu] autograd {dtype} q={separate_q}", flush=True)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps, chunk_row=wl.chunk_row,
+              chunk_col=wl.chunk_col)
+    x = torch.from_numpy(wl.x).to(DEV).to(dt).requires_grad_()
+    q = None if wl.q is None else torch.from_numpy(wl.q).to(DEV).to(dt).requires_grad_()
+    st = torch.from_numpy(wl.states).to(DEV).requires_grad_()
+    sc = torch.from_numpy(wl.scales).to(DEV).requires_grad_()
+    out = srnl.operator(x, st, sc, wl.heads, wl.d, 15, q, **kw)
+    with torch.no_grad():
+        ref_out = srnl.forward(x.detach(), st.detach(), sc.detach(), wl.heads, wl.d, 15,
+                               None if q is None else q.detach(), **kw)
+    assert out.dtype == dt and torch.equal(out, ref_out)
+    g = torch.from_numpy(np.random.default_rng(9).standard_normal(out.shape)
+                         .astype(np.float32)).to(DEV).to(dt)
+    out.backward(g)
+    torch.cuda.synchronize()
+    R = 4
+    gx, gq, gst, gsc = G.grads(wl.x, wl.states, wl.scales, wl.heads, wl.d, 15, wl.q,
+                               dy=np.zeros((R, wl.B, wl.N, wl.C), np.float32),
+                               dfused=g.float().cpu().numpy(), **_kw(wl, 0))
+
+    def close(got, ref, name):
+        got = got.float().cpu().numpy()
+        if dt == torch.bfloat16 and name in ("dx", "dq"):
+            bound = 2.0 ** -8 * np.abs(ref) + TOL * np.abs(ref).max()
+            assert (np.abs(got - ref) <= bound).all(), name
+        else:
+            assert rel(got, ref) <= TOL, name
+
+    assert x.grad.dtype == dt
+    close(x.grad, gx, "dx")
+    close(st.grad, gst, "dst")
+    close(sc.grad, gsc, "dsc")
+    if q is not None:
+        close(q.grad, gq, "dq")

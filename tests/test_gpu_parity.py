@@ -500,3 +500,57 @@ def test_misaligned_tensors_are_pointer_errors():
     # the aligned calls still work
     srnl.fuse(y, B, H, W, C, 15, sc)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_check_finite_flag(dtype):
+    """SRNL_FLAG_CHECK_FINITE: on finite inputs the outputs equal an unchecked
+    call's bit for bit; a NaN or an Inf in x or in the separate queries makes
+    the call return SRNL_ERR_NONFINITE with the number of such values."""
+    print(f"[gpu] check_finite {dtype}", flush=True)
+    wl = synth.make("fin", 2, 6, 7, 64, 2, 32, dtype, 61)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(wl.x).to(DEV).to(dt)
+    st = torch.from_numpy(wl.states).to(DEV)
+    flag = srnl.FLAG_CHECK_FINITE
+    y0 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15)
+    y1 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, flags=flag)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+    xb = x.clone()
+    xb.view(-1)[5] = float("nan")
+    xb.view(-1)[-1] = float("inf")
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd(xb, st, wl.heads, wl.d, 15, flags=flag)
+    assert e.value.status == srnl.SRNL_ERR_NONFINITE
+    assert "2 non-finite input values" in str(e.value)
+
+    q = x.clone()
+    q.view(-1)[100] = float("-inf")
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd(x, st, wl.heads, wl.d, 15, q=q, flags=flag)
+    assert e.value.status == srnl.SRNL_ERR_NONFINITE
+    assert "1 non-finite input values" in str(e.value)
+
+    # a caller's workspace: too small is an error; a valid one is cleared on
+    # every call, so a clean call after a failing one succeeds
+    p = srnl.make_params(st, x, flags=flag)
+    small = torch.empty(8, dtype=torch.uint8, device=DEV)
+    p.workspace, p.workspace_bytes = small.data_ptr(), 8
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd(x, st, wl.heads, wl.d, 15, params=p)
+    assert e.value.status == srnl.SRNL_ERR_WORKSPACE
+    nb = srnl.lib().srnl_scan_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                              ctypes.byref(p))
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    p.workspace, p.workspace_bytes = ws.data_ptr(), nb
+    with pytest.raises(srnl.SrnlError):
+        srnl.scan_fwd(xb, st, wl.heads, wl.d, 15, params=srnl.make_params(st, xb, flags=flag))
+    pb = srnl.make_params(st, xb, flags=flag)
+    pb.workspace, pb.workspace_bytes = ws.data_ptr(), nb
+    with pytest.raises(srnl.SrnlError):
+        srnl.scan_fwd(xb, st, wl.heads, wl.d, 15, params=pb)
+    y2 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, params=p)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y2)
