@@ -220,3 +220,39 @@ def test_autograd_operator(dtype, separate_q):
     close(sc.grad, gsc, "dsc")
     if q is not None:
         close(q.grad, gq, "dq")
+
+
+def test_grad_hier56_bench_launch_sampled_items():
+    """The backward in the benchmark's launch configuration (56x56, B = 64,
+    C = 64, 2 heads x d = 32, bf16, four routes). dx of items 0 and 63 is
+    checked against the oracle on those items. The state and scale
+    gradients are sums over the batch; by linearity in the output gradient,
+    the full run's minus that of a second run whose output gradient is zero
+    on items 0 and 63 is the two items' share, checked against the oracle."""
+    wl = synth.hier56()
+    print(f"[gpu] grad hier56 B={wl.B} sampled items", flush=True)
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps, chunk_row=wl.chunk_row,
+              chunk_col=wl.chunk_col)
+    x = torch.from_numpy(wl.x).to(DEV).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(DEV)
+    sc = torch.from_numpy(wl.scales).to(DEV)
+    sel = [0, wl.B - 1]
+    dout = np.random.default_rng(11).standard_normal((wl.B, wl.H, wl.W, wl.C)).astype(np.float32)
+    rest = dout.copy()
+    rest[sel] = 0.0
+    y = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, **kw)
+    out = []
+    for g in (dout, rest):
+        dyr, dsc = srnl.fuse_bwd(torch.from_numpy(g).to(DEV), y, wl.B, wl.H, wl.W, wl.C, 15, sc)
+        dx, _, dst = srnl.scan_bwd(x, st, wl.heads, wl.d, dyr, 15, **kw)
+        out.append((dx.cpu().numpy(), dst.cpu().numpy().astype(np.float64),
+                    dsc.cpu().numpy().astype(np.float64)))
+    torch.cuda.synchronize()
+    gx, _, gst, gsc = G.grads(wl.x[sel], wl.states, wl.scales, wl.heads, wl.d, 15, None,
+                              dy=np.zeros((4, 2, wl.N, wl.C), np.float32), dfused=dout[sel],
+                              **_kw(wl, 0))
+    assert np.isfinite(out[0][0]).all()
+    assert rel(out[0][0][sel], gx) <= TOL, "dx"
+    assert rel(out[0][1] - out[1][1], gst) <= TOL, "dstates"
+    assert rel(out[0][2] - out[1][2], gsc) <= TOL, "dscales"
+    assert not out[1][0][sel].any()     # zero output gradient, zero dx

@@ -426,6 +426,26 @@ def test_scan_1d_matches_oracle(d, dtype, chunk):
     assert chunk_rel(yg, yo, chunk if chunk > 0 else 64) <= TOL_CHUNK
 
 
+def test_scan_1d_bench_workload_sampled():
+    """The 1-D benchmark workload in its launch configuration (256 sequences
+    of 3136 tokens, 2 heads x d = 32, bf16, 64-token chunks); sequences are
+    independent, so the oracle checks the first and the last."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                              "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    x, st, heads, d = bench.seq1d_workload()
+    yg = _scan_1d_gpu(x, st, heads, d, dtype="bf16")
+    sel = [0, x.shape[0] - 1]
+    yo = oracle.scan_1d(x[sel], st, heads, d)
+    assert np.isfinite(yg).all()
+    assert rel(yg[sel], yo) <= TOL32
+    assert chunk_rel(yg[sel], yo, 64) <= TOL_CHUNK
+
+
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 1000])
 def test_scan_1d_lengths(N):
     B, C, heads, d = 3, 64, 2, 32
