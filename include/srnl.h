@@ -20,8 +20,9 @@
  *
  * Conventions for every entry point:
  *   - Tensors are device pointers (HBM) unless a comment says "host". The
- *     caller allocates and owns every buffer; the library never allocates,
- *     frees or synchronises, and keeps no state between calls.
+ *     caller allocates and owns every buffer; the library never allocates
+ *     or frees, keeps no state between calls, and does not wait for the
+ *     stream (except under SRNL_FLAG_CHECK_FINITE).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously: a return of SRNL_OK means the arguments were
  *     valid and the kernels were launched.
@@ -139,7 +140,9 @@ typedef struct {
  * negative sizes, alpha_max not in (0,1), eps <= 0, negative chunk,
  * sizes whose element counts overflow), SRNL_ERR_DTYPE, SRNL_ERR_PTR
  * (x, out or params->states NULL or not device memory; q not device
- * memory), SRNL_ERR_HIP.
+ * memory), SRNL_ERR_HIP; with SRNL_FLAG_CHECK_FINITE also SRNL_ERR_WORKSPACE
+ * (workspace NULL or too small) and SRNL_ERR_NONFINITE (the detail string
+ * gives the counts of non-finite inputs and outputs).
  */
 srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
                           int d, unsigned route_mask, const srnl_params *params,
@@ -149,7 +152,8 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
  * srnl_scan_workspace_bytes -- device workspace srnl_scan_fwd needs for these
  * sizes and params: 0 unless params->flags has SRNL_FLAG_CHECK_FINITE (then
  * room for two counters, non-finite input and output values). 0 for an
- * empty grid or invalid arguments.
+ * empty grid or invalid arguments. For srnl_scan_1d on [B, N, C] pass
+ * H = 1, W = N and route_mask = SRNL_ROUTE_ROW.
  */
 size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
                                  unsigned route_mask, const srnl_params *params);

@@ -1455,7 +1455,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 __device__ __forceinline__ unsigned nonfinite(float v) { return (__float_as_uint(v) & 0x7F800000u) == 0x7F800000u; }
 __device__ __forceinline__ unsigned nonfinite(uint16_t v) { return (v & 0x7F80u) == 0x7F80u; }
 
-// counters[0..1] = 0 (a kernel rather than a memset, so the call can be captured)
+// counters[0..1] = 0, enqueued on the stream like the counting kernels
 __global__ void zero_counters_kernel(unsigned *__restrict__ counters)
 {
     if (threadIdx.x < 2)

@@ -168,6 +168,20 @@ def make_params(states: torch.Tensor, x: torch.Tensor, q: Optional[torch.Tensor]
                   chunk_col, flags, _stream(stream))
 
 
+def _finite_check_workspace(p: Params, x: torch.Tensor, B, H, W, C, heads, d, route_mask):
+    """With SRNL_FLAG_CHECK_FINITE and no caller workspace, allocate one and
+    point p at it; the call waits for its stream when checking, so the buffer
+    outlives its use. Returns the tensor (None when nothing was allocated)."""
+    if not (p.flags & FLAG_CHECK_FINITE) or p.workspace:
+        return None
+    nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
+    if not nbytes:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
+    return ws
+
+
 def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
              route_mask: int = 15, q: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, *, params: Optional[Params] = None,
@@ -180,14 +194,7 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
     _expect(out, (R, B, H * W, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, **kw)
-    ws = None
-    if p.flags & FLAG_CHECK_FINITE and not p.workspace:
-        # the call waits for the stream when checking, so the buffer outlives its use
-        nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask,
-                                                 ctypes.byref(p))
-        if nbytes:
-            ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
-            p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
+    ws = _finite_check_workspace(p, x, B, H, W, C, heads, d, route_mask)
     try:
         _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
                                    ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
@@ -207,8 +214,13 @@ def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         out = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
     _expect(out, (B, N, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, chunk_row=chunk, **kw)
-    _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
-           "srnl_scan_1d")
+    ws = _finite_check_workspace(p, x, B, 1, N, C, heads, d, 1)
+    try:
+        _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
+               "srnl_scan_1d")
+    finally:
+        if ws is not None:
+            p.workspace, p.workspace_bytes = None, 0
     return out
 
 

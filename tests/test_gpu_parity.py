@@ -574,3 +574,22 @@ def test_check_finite_flag(dtype):
     y2 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, params=p)
     torch.cuda.synchronize()
     assert torch.equal(y0, y2)
+
+
+def test_check_finite_flag_1d():
+    """srnl_scan_1d takes the same finite check as the 2-D scan."""
+    print("[gpu] check_finite 1d", flush=True)
+    x, st, _ = _seq(2, 100, 64, 2, 32, seed=62, dtype="bf16")
+    xg = _dev(x, torch.bfloat16)
+    stg = _dev(st, torch.float32)
+    flag = srnl.FLAG_CHECK_FINITE
+    y0 = srnl.scan_1d(xg, stg, 2, 32)
+    y1 = srnl.scan_1d(xg, stg, 2, 32, flags=flag)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    xb = xg.clone()
+    xb[1, 50, 7] = float("nan")
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_1d(xb, stg, 2, 32, flags=flag)
+    assert e.value.status == srnl.SRNL_ERR_NONFINITE
+    assert "1 non-finite input values" in str(e.value)
