@@ -140,6 +140,20 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _keep_for_stream(handle, *tensors) -> None:
+    """Temporaries this binding allocates (on the current stream) and frees
+    on return, but whose kernels run on the stream ``handle``: record that
+    stream on them, so the caching allocator does not hand their memory out
+    again before that stream's work is done."""
+    cur = torch.cuda.current_stream()
+    if (handle or 0) == (cur.cuda_stream or 0):
+        return
+    s = torch.cuda.ExternalStream(handle) if handle else torch.cuda.default_stream()
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return SRNL_F32
@@ -256,6 +270,7 @@ def scan_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torc
     _check(lib().srnl_scan_bwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
                                _ptr(dy), _ptr(ws), int(nbytes), _ptr(dx), _ptr(dq), _ptr(dst)),
            "srnl_scan_bwd")
+    _keep_for_stream(p.stream, ws)
     return dx, dq, dst
 
 
@@ -270,9 +285,11 @@ def fuse_bwd(dout: torch.Tensor, y: torch.Tensor, B: int, H: int, W: int, C: int
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dout.device)
     dyr = torch.empty_like(y)
     dsc = torch.empty((4, C), dtype=torch.float32, device=dout.device)
+    sh = _stream(stream)
     _check(lib().srnl_fuse_bwd(_ptr(dout), _ptr(y), B, H, W, C, route_mask, _ptr(scales),
-                               _ptr(dyr), _ptr(dsc), _ptr(ws), int(nbytes), _stream(stream)),
+                               _ptr(dyr), _ptr(dsc), _ptr(ws), int(nbytes), sh),
            "srnl_fuse_bwd")
+    _keep_for_stream(sh, ws)
     return dyr, dsc
 
 
@@ -320,7 +337,7 @@ class Operator(torch.autograd.Function):
     def forward(ctx, x, states, scales, q, heads, d, route_mask, kw):
         B, H, W, C = x.shape
         y = scan_fwd(x, states, heads, d, route_mask, q, **kw)
-        out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype)
+        out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype, stream=kw.get("stream"))
         ctx.save_for_backward(x, states, scales, q, y)
         ctx.cfg = (heads, d, route_mask, kw)
         return out
@@ -331,7 +348,7 @@ class Operator(torch.autograd.Function):
         heads, d, route_mask, kw = ctx.cfg
         B, H, W, C = x.shape
         dout = dout.to(torch.float32).contiguous()
-        dyr, dsc = fuse_bwd(dout, y, B, H, W, C, route_mask, scales)
+        dyr, dsc = fuse_bwd(dout, y, B, H, W, C, route_mask, scales, stream=kw.get("stream"))
         dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, **kw)
         return (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype),
                 None, None, None, None)
@@ -385,11 +402,14 @@ def block_fwd(x: torch.Tensor, states: torch.Tensor, weights: BlockWeights, head
     nbytes = lib().srnl_block_workspace_bytes(B, H, W, C, route_mask)
     if workspace is not None and workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace smaller than srnl_block_workspace_bytes")
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
     p = params if params is not None else make_params(states, x, **kw)
     _check(lib().srnl_block_fwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
                                 ctypes.byref(weights), _ptr(workspace),
                                 int(workspace.numel() * workspace.element_size()),
                                 _ptr(out)), "srnl_block_fwd")
+    if own:
+        _keep_for_stream(p.stream, workspace)
     return out

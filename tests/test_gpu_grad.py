@@ -256,3 +256,28 @@ def test_grad_hier56_bench_launch_sampled_items():
     assert rel(out[0][1] - out[1][1], gst) <= TOL, "dstates"
     assert rel(out[0][2] - out[1][2], gsc) <= TOL, "dscales"
     assert not out[1][0][sel].any()     # zero output gradient, zero dx
+
+
+def test_backward_on_a_side_stream_matches():
+    """The backward entry points and the block launched on a stream other
+    than the current one (the binding's temporaries are recorded on it)
+    give bitwise the results of the current-stream calls."""
+    print("[gpu] side-stream backward and block", flush=True)
+    wl = _wl("gside", 2, 6, 7, 2, 32, dtype="bf16", seed=12)
+    x = torch.from_numpy(wl.x).to(DEV).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(DEV)
+    sc = torch.from_numpy(wl.scales).to(DEV)
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps)
+    dout = torch.from_numpy(np.random.default_rng(12).standard_normal(
+        (wl.B, wl.H, wl.W, wl.C)).astype(np.float32)).to(DEV)
+    y = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, **kw)
+    ref_dy, ref_dsc = srnl.fuse_bwd(dout, y, wl.B, wl.H, wl.W, wl.C, 15, sc)
+    ref = srnl.scan_bwd(x, st, wl.heads, wl.d, ref_dy, 15, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    dy, dsc = srnl.fuse_bwd(dout, y, wl.B, wl.H, wl.W, wl.C, 15, sc, stream=side)
+    side.synchronize()
+    got = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15, stream=side, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dy, ref_dy) and torch.equal(dsc, ref_dsc)
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[2], ref[2])
