@@ -504,6 +504,45 @@ def main_hier56_bwd(args):
     dt = time.perf_counter() - t0
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms = dt * 1000.0 / args.steps
+
+    # One training step of the operator (forward scan + fuse, fusion backward,
+    # scan backward), once with the forward keeping its record for the
+    # backward (SRNL_FLAG_RECORD) and once with the backward recording it again.
+    pr = srnl.make_params(st, x, flags=srnl.FLAG_RECORD)
+    nb_r = L.srnl_scan_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                       ctypes.byref(pr))
+    ws_r = torch.empty(nb_r, dtype=torch.uint8, device=dev)
+    pr.workspace, pr.workspace_bytes = ws_r.data_ptr(), nb_r
+    nb_sr = L.srnl_scan_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                            ctypes.byref(pr))
+    ws_sr = torch.empty(nb_sr, dtype=torch.uint8, device=dev)
+    fused = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.bfloat16, device=dev)
+
+    def train(record):
+        pp, ws, nb = (pr, ws_sr, nb_sr) if record else (p, ws_s, nb_s)
+        rc = L.srnl_scan_fwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                             ctypes.byref(pp), y.data_ptr())
+        rc |= L.srnl_fuse(y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15, sc.data_ptr(),
+                          srnl.SRNL_BF16, fused.data_ptr(), stream)
+        rc |= L.srnl_fuse_bwd(dout.data_ptr(), y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15,
+                              sc.data_ptr(), dyr.data_ptr(), dsc.data_ptr(), ws_f.data_ptr(),
+                              nb_f, stream)
+        rc |= L.srnl_scan_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                              ctypes.byref(pp), dyr.data_ptr(), ws.data_ptr(), nb,
+                              dx.data_ptr(), None, dst.data_ptr())
+        if rc != 0:
+            raise RuntimeError("training step failed")
+
+    train_ms = {True: None, False: None}
+    for record in (() if args.no_train_step else (True, False)):
+        for _ in range(args.warmup):
+            train(record)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            train(record)
+        torch.cuda.synchronize()
+        train_ms[record] = (time.perf_counter() - t1) * 1000.0 / args.steps
     units = wl.B * wl.H * wl.W * wl.heads
     flops = 2 * algorithmic_flops_per_unit(wl.d) * units * R
     achieved = flops / (scan_ms / 1000.0) / 1e12
@@ -525,6 +564,11 @@ def main_hier56_bwd(args):
                      "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
                      "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None,
+        "train_step": {"what": "srnl_scan_fwd + srnl_fuse (bf16 out) + srnl_fuse_bwd + "
+                               "srnl_scan_bwd per step",
+                       "ms_forward_keeps_record": train_ms[True],
+                       "ms_backward_records_again": train_ms[False],
+                       "record_bytes": nb_r},
     }
     print(json.dumps(rec), flush=True)
 
@@ -537,6 +581,9 @@ def main():
     ap.add_argument("--cpu-items", type=int, default=64,
                     help="batch items the CPU-baseline oracle runs on (64 = the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="hier56_bwd: skip the training-step timing (kernel traces of the "
+                         "backward alone)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--pmc-summary", metavar="DIR",

@@ -83,6 +83,15 @@ typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
  * a workspace of srnl_scan_workspace_bytes, and the call then waits for its
  * stream to finish. Other entry points ignore the flag. */
 #define SRNL_FLAG_CHECK_FINITE 0x40u
+/* Keep the forward's record for the backward pass (training). srnl_scan_fwd
+ * also writes, into params->workspace, the per-chain record that the
+ * windowed backward reads (each chunk's boundary rows and closing Q, and each
+ * 16-token window's opening Q, u rows and transition scalars); srnl_scan_bwd
+ * called with the same arguments, flags and workspace then reads that record
+ * instead of recomputing it. Applies where the windowed backward does: d = 32
+ * with the readout after the write; elsewhere, and in the other entry points,
+ * the flag changes nothing. The record takes srnl_scan_workspace_bytes. */
+#define SRNL_FLAG_RECORD 0x80u
 
 /* Floats of initial state per (route, head): 3d^2 + 2d. */
 #define SRNL_STATE_FLOATS(d) (3 * (d) * (d) + 2 * (d))
@@ -107,7 +116,9 @@ typedef struct {
     void *stream;         /* hipStream_t */
     /* Device workspace for srnl_scan_fwd / srnl_scan_1d, at least
      * srnl_scan_workspace_bytes(...) bytes (that is 0, and this may be NULL,
-     * unless SRNL_FLAG_CHECK_FINITE is set); caller-owned, contents scratch. */
+     * unless SRNL_FLAG_CHECK_FINITE or SRNL_FLAG_RECORD is set), 16-byte
+     * aligned; caller-owned. With SRNL_FLAG_RECORD it starts with the forward
+     * record, which srnl_scan_bwd reads from here; otherwise scratch. */
     void *workspace;
     size_t workspace_bytes;
 } srnl_params;
@@ -149,10 +160,11 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
                           float *out);
 
 /*
- * srnl_scan_workspace_bytes -- device workspace srnl_scan_fwd needs for these
- * sizes and params: 0 unless params->flags has SRNL_FLAG_CHECK_FINITE (then
- * room for two counters, non-finite input and output values). 0 for an
- * empty grid or invalid arguments. For srnl_scan_1d on [B, N, C] pass
+ * srnl_scan_workspace_bytes -- device workspace srnl_scan_fwd needs in
+ * params->workspace for these sizes and params: the forward record under
+ * SRNL_FLAG_RECORD (where it applies), then 256 bytes for two counters
+ * (non-finite input and output values) under SRNL_FLAG_CHECK_FINITE; 0
+ * without either flag, for an empty grid or for invalid arguments. For srnl_scan_1d on [B, N, C] pass
  * H = 1, W = N and route_mask = SRNL_ROUTE_ROW.
  */
 size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
@@ -215,7 +227,10 @@ srnl_status srnl_fuse(const float *y_routes, int B, int H, int W, int C,
  * per chain, every chunk's boundary and closing state and every 16-token
  * window's opening state, update rows and transition scalars into the
  * workspace; the adjoint then walks the chunks and windows backwards, 16
- * tokens at a time. Otherwise each chain re-runs the forward to record the
+ * tokens at a time. With SRNL_FLAG_RECORD the record comes instead from
+ * params->workspace, written by srnl_scan_fwd with the same arguments and
+ * params, and the workspace here holds only the rest (smaller
+ * srnl_scan_bwd_workspace_bytes). Otherwise each chain re-runs the forward to record the
  * boundary of every chunk, then walks the chunks backwards, re-running each
  * chunk to record the working state after every token, and walks the tokens
  * backwards. Sums run in a fixed order (bitwise reproducible).

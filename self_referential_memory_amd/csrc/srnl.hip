@@ -152,7 +152,8 @@ template <int D> struct ScanCfg {
 
 enum : unsigned {
     F_HARD_CAP = 0x1u, F_NO_CAP = 0x2u, F_NO_CLAMP = 0x4u, F_FIXED_ALPHA = 0x8u,
-    F_READ_BEFORE = 0x10u, F_FREEZE_KV = 0x20u, F_CHECK_FINITE = 0x40u
+    F_READ_BEFORE = 0x10u, F_FREEZE_KV = 0x20u, F_CHECK_FINITE = 0x40u,
+    F_RECORD = 0x80u
 };
 
 template <int D, typename InT>
@@ -726,7 +727,8 @@ template <int D> struct SaveLayout {
 // branch bits of a recorded token: soft-cap series, hard cap taken, clamp taken
 constexpr int SCB_SERIES = 1, SCB_HARD = 2, SCB_CLAMP = 4;
 
-template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false>
+template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false,
+          bool OUT = !SAVE>
 __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
@@ -1350,7 +1352,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     tm = w, w + NW, ... and writes whole output rows of its head;
         //     otherwise wave w takes the channel tiles tn = w, w + NW, ... for
         //     every token tile.
-        if constexpr (!SAVE) {
+        if constexpr (OUT) {
             constexpr bool BY_TOKENS = NW > NTC;
             const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
             const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
@@ -1726,9 +1728,9 @@ int longest_chunk(int H, int W, unsigned mask, int chunk_row, int chunk_col)
     return static_cast<int>(L);
 }
 
-// With SAVE the kernel writes no route outputs but the record FwdSave sv
-// for the windowed backward (readout after the write only).
-template <int D, int T, typename InT, bool SAVE = false>
+// With SAVE the kernel writes the record FwdSave sv for the windowed
+// backward (readout after the write only), and the route outputs too with OUT.
+template <int D, int T, typename InT, bool SAVE = false, bool OUT = !SAVE>
 void launch_scan_mfma(const void *x, const srnl_params *p, int B, int H, int W, int C,
                       int heads, unsigned mask, int R, int nchains, int nblocks, float *out,
                       FwdSave sv = FwdSave())
@@ -1743,8 +1745,8 @@ void launch_scan_mfma(const void *x, const srnl_params *p, int B, int H, int W, 
                            p->chunk_row, p->chunk_col, p->flags, nchains, sv);
     };
     if constexpr (SAVE) {
-        has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT, true>)
-              : go(scan_mfma_kernel<D, NW, T, false, false, InT, true>);
+        has_q ? go(scan_mfma_kernel<D, NW, T, false, true, InT, true, OUT>)
+              : go(scan_mfma_kernel<D, NW, T, false, false, InT, true, OUT>);
     } else if (before) {
         has_q ? go(scan_mfma_kernel<D, NW, T, true, true, InT>)
               : go(scan_mfma_kernel<D, NW, T, true, false, InT>);
@@ -1787,6 +1789,40 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
     }
 }
 
+// The recording forward at d = 32 (readout after the write): the record sv
+// of every chain for the windowed backward, and the route outputs when out
+// is not NULL. The sub-block follows the longest chunk.
+template <typename InT>
+srnl_status launch_record_fwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
+                              int heads, unsigned mask, float *out, const FwdSave &sv)
+{
+    const int R = popcount4(mask);
+    const long long nchains = static_cast<long long>(R) * B * heads;
+    if (nchains > INT_MAX - 8)
+        return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
+    const int nc = static_cast<int>(nchains);
+    const int nblocks = (nc + 7) / 8 * 8;
+    const int L = longest_chunk(H, W, mask, p->chunk_row, p->chunk_col);
+    auto go = [&](auto t, auto o) {
+        constexpr int T = decltype(t)::value;
+        constexpr bool O = decltype(o)::value;
+        launch_scan_mfma<32, T, InT, true, O>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out, sv);
+    };
+    auto pick = [&](auto o) {
+        if (L <= 16)
+            go(std::integral_constant<int, 16>(), o);
+        else if (L <= 32)
+            go(std::integral_constant<int, 32>(), o);
+        else
+            go(std::integral_constant<int, 64>(), o);
+    };
+    if (out)
+        pick(std::true_type());
+    else
+        pick(std::false_type());
+    return launch_check("scan_mfma_kernel (forward record)");
+}
+
 template <typename InT>
 srnl_status dispatch_scan(int d, const void *x, const srnl_params *p, int B, int H, int W,
                           int C, int heads, unsigned mask, float *out)
@@ -1820,14 +1856,51 @@ srnl_status check_grid(int B, int H, int W, int C, unsigned mask, long long *n_o
 // per-chain scratch, per-route dx partials, per-route dq partials, per-chain
 // initial-state gradients.
 struct BwdLayout {
-    long long chain_floats = 0, chains = 0, o_dx = 0, o_dq = 0, o_st = 0, total = 0;
-};
+    long long chain_floats = 0, chains = 0, o_dx = 0, o_dq = 0, o_st = 0, total = -1;
+    bool record_given = false;   // the forward record comes in params->workspace
+};   // total < 0: the sizes overflow
 
 long long align64(long long n) { return (n + 63) / 64 * 64; }
 
 // The windowed backward (d = 32, readout after the write) reads a record of
 // the forward instead of re-running it token by token.
 bool bwd_windowed(int d, const srnl_params *p) { return d == 32 && !(p->flags & F_READ_BEFORE); }
+
+// Floats of one chain's forward record (the longest over the active routes),
+// 64-float aligned.
+long long record_chain_floats(int H, int W, unsigned mask, const srnl_params *p)
+{
+    const long long N = static_cast<long long>(H) * W;
+    long long m = 0;
+    for (int r = 0; r < 4; ++r) {
+        if (!(mask & (1u << r)))
+            continue;
+        long long L = (r < 2) ? (p->chunk_row > 0 ? p->chunk_row : W)
+                              : (p->chunk_col > 0 ? p->chunk_col : H);
+        if (L > N)
+            L = N;
+        if (L < 1)
+            L = 1;
+        const long long f = SaveLayout<32>{(N + L - 1) / L, (L + 15) / 16}.floats();
+        if (f > m)
+            m = f;
+    }
+    return align64(m);
+}
+
+// Bytes of the record SRNL_FLAG_RECORD asks for (0 where the windowed
+// backward does not apply), 256-byte aligned; -1 past 2^62 bytes.
+long long record_bytes(int B, int H, int W, int heads, int d, unsigned mask, const srnl_params *p)
+{
+    if (!(p->flags & F_RECORD) || !bwd_windowed(d, p))
+        return 0;
+    const long long chains = static_cast<long long>(popcount4(mask)) * B * heads;
+    long long f = 0;
+    if (__builtin_mul_overflow(chains, record_chain_floats(H, W, mask, p), &f) ||
+        f > (1LL << 60) - 64)
+        return -1;
+    return (f * 4 + 255) / 256 * 256;
+}
 
 BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask,
                      const srnl_params *p)
@@ -1854,11 +1927,18 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
     }
     l.chain_floats = align64(l.chain_floats);
     l.chains = static_cast<long long>(R) * B * heads;
+    l.record_given = wy && (p->flags & F_RECORD);
     const long long part = align64(static_cast<long long>(R) * B * N * C);
-    l.o_dx = l.chains * l.chain_floats;
+    long long rec = 0;
+    if (!l.record_given && __builtin_mul_overflow(l.chains, l.chain_floats, &rec))
+        return l;
+    l.o_dx = rec;
     l.o_dq = l.o_dx + part;
     l.o_st = l.o_dq + (p->q ? part : 0);
-    l.total = l.o_st + align64(l.chains * rows * d);
+    const long long t = l.o_st + align64(l.chains * rows * d);
+    if (rec > (1LL << 60) || t > (1LL << 60))
+        return l;
+    l.total = t;
     return l;
 }
 
@@ -1880,22 +1960,16 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
     srnl_status s;
     if constexpr (D == 32) {
         if (bwd_windowed(D, p)) {
-            // the forward record, then the windowed backward
+            // the forward record (from the caller's forward, or recorded
+            // here), then the windowed backward
             const int nblocks = (nchains + 7) / 8 * 8;
-            const FwdSave sv{ws, l.chain_floats};
-            const int L = longest_chunk(H, W, mask, p->chunk_row, p->chunk_col);
-            if (L <= 16)
-                launch_scan_mfma<D, 16, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
-                                                   nblocks, nullptr, sv);
-            else if (L <= 32)
-                launch_scan_mfma<D, 32, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
-                                                   nblocks, nullptr, sv);
-            else
-                launch_scan_mfma<D, 64, InT, true>(x, p, B, H, W, C, heads, mask, R, nchains,
-                                                   nblocks, nullptr, sv);
-            s = launch_check("scan_mfma_kernel (forward record)");
-            if (s != SRNL_OK)
-                return s;
+            const FwdSave sv{l.record_given ? static_cast<float *>(p->workspace) : ws,
+                             l.chain_floats};
+            if (!l.record_given) {
+                s = launch_record_fwd<InT>(x, p, B, H, W, C, heads, mask, nullptr, sv);
+                if (s != SRNL_OK)
+                    return s;
+            }
             auto gw = [&](auto kern) {
                 hipLaunchKernelGGL(kern, dim3(nblocks), dim3(wyb::NT), 0, st,
                                    static_cast<const InT *>(x), static_cast<const InT *>(p->q), dy,
@@ -1972,7 +2046,7 @@ srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsign
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x7Fu)
+    if (p->flags & ~0xFFu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
@@ -2065,12 +2139,15 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_ARG, "eps must be positive and finite");
     if (p->chunk_row < 0 || p->chunk_col < 0)
         return fail(SRNL_ERR_ARG, "chunk lengths must be >= 0");
-    if (p->flags & ~0x7Fu)
+    if (p->flags & ~0xFFu)
         return fail(SRNL_ERR_ARG, "unknown flag bits");
     if (p->in_dtype != SRNL_F32 && p->in_dtype != SRNL_BF16)
         return fail(SRNL_ERR_DTYPE, "in_dtype must be SRNL_F32 or SRNL_BF16");
     if (n == 0)
         return SRNL_OK;   // empty grid
+    const long long rec = record_bytes(B, H, W, heads, d, route_mask, p);
+    if (rec < 0)
+        return fail(SRNL_ERR_ARG, "grid too large for SRNL_FLAG_RECORD");
     if (!is_device_ptr(x) || !is_device_ptr(out) || !is_device_ptr(p->states))
         return fail(SRNL_ERR_PTR, "x, out and states must be device memory");
     if (p->q && !is_device_ptr(p->q))
@@ -2078,12 +2155,16 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
     if (!aligned16(x) || !aligned16(out) || !aligned16(p->states) || (p->q && !aligned16(p->q)))
         return fail(SRNL_ERR_PTR, "x, q, out and states must be 16-byte aligned");
     const bool check = (p->flags & F_CHECK_FINITE) != 0;
-    unsigned *counters = static_cast<unsigned *>(p->workspace);
-    if (check) {
-        if (!counters || p->workspace_bytes < kScanCheckBytes)
-            return fail(SRNL_ERR_WORKSPACE, "SRNL_FLAG_CHECK_FINITE needs srnl_scan_workspace_bytes of workspace");
-        if (!is_device_ptr(counters))
-            return fail(SRNL_ERR_PTR, "workspace must be device memory");
+    // workspace: the forward record (SRNL_FLAG_RECORD), then the counters
+    const size_t need = static_cast<size_t>(rec) + (check ? kScanCheckBytes : 0);
+    unsigned *counters = nullptr;
+    if (need > 0) {
+        if (!p->workspace || p->workspace_bytes < need)
+            return fail(SRNL_ERR_WORKSPACE, "params->workspace smaller than srnl_scan_workspace_bytes");
+        if (!is_device_ptr(p->workspace) || !aligned16(p->workspace))
+            return fail(SRNL_ERR_PTR, "params->workspace must be 16-byte aligned device memory");
+        if (check)
+            counters = reinterpret_cast<unsigned *>(static_cast<char *>(p->workspace) + rec);
     }
     hipStream_t st = static_cast<hipStream_t>(p->stream);
     const long long nx = static_cast<long long>(B) * H * W * C;
@@ -2106,9 +2187,16 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
         if (s != SRNL_OK)
             return s;
     }
-    s = (p->in_dtype == SRNL_F32)
-            ? dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out)
-            : dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
+    if (rec > 0) {
+        const FwdSave sv{static_cast<float *>(p->workspace), record_chain_floats(H, W, route_mask, p)};
+        s = (p->in_dtype == SRNL_F32)
+                ? launch_record_fwd<float>(x, p, B, H, W, C, heads, route_mask, out, sv)
+                : launch_record_fwd<uint16_t>(x, p, B, H, W, C, heads, route_mask, out, sv);
+    } else {
+        s = (p->in_dtype == SRNL_F32)
+                ? dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out)
+                : dispatch_scan<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, out);
+    }
     if (s != SRNL_OK || !check)
         return s;
     hipLaunchKernelGGL(nonfinite_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, out, n,
@@ -2134,7 +2222,10 @@ size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
     if (!p || !valid_d(d) || heads < 1 || C != heads * d ||
         check_grid(B, H, W, C, route_mask, &n) != SRNL_OK || n == 0)
         return 0;
-    return (p->flags & F_CHECK_FINITE) ? kScanCheckBytes : 0;
+    const long long rec = record_bytes(B, H, W, heads, d, route_mask, p);
+    if (rec < 0)
+        return 0;
+    return static_cast<size_t>(rec) + ((p->flags & F_CHECK_FINITE) ? kScanCheckBytes : 0);
 }
 
 srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
@@ -2184,7 +2275,8 @@ size_t srnl_scan_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int 
     long long n = 0;
     if (check_scan_args(B, H, W, C, heads, d, route_mask, p, &n) != SRNL_OK || n == 0)
         return 0;
-    return static_cast<size_t>(bwd_layout(B, H, W, C, heads, d, route_mask, p).total) * sizeof(float);
+    const long long t = bwd_layout(B, H, W, C, heads, d, route_mask, p).total;
+    return t < 0 ? 0 : static_cast<size_t>(t) * sizeof(float);
 }
 
 srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
@@ -2200,6 +2292,8 @@ srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, 
     if (n == 0)
         return SRNL_OK;   // empty grid
     const BwdLayout l = bwd_layout(B, H, W, C, heads, d, route_mask, p);
+    if (l.total < 0)
+        return fail(SRNL_ERR_ARG, "grid too large for srnl_scan_bwd's workspace");
     if (!workspace || workspace_bytes < static_cast<size_t>(l.total) * sizeof(float))
         return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_scan_bwd_workspace_bytes");
     if (!is_device_ptr(x) || !is_device_ptr(p->states) || !is_device_ptr(dy) ||
@@ -2212,6 +2306,15 @@ srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, 
         return fail(SRNL_ERR_PTR, "x, q, states, dy, dx, dq, dstates and workspace must be 16-byte aligned");
     if (l.chains > INT_MAX)
         return fail(SRNL_ERR_ARG, "too many chains (routes * B * heads)");
+    if (l.record_given) {
+        const long long rec = record_bytes(B, H, W, heads, d, route_mask, p);
+        if (rec < 0)
+            return fail(SRNL_ERR_ARG, "grid too large for SRNL_FLAG_RECORD");
+        if (!p->workspace || p->workspace_bytes < static_cast<size_t>(rec))
+            return fail(SRNL_ERR_WORKSPACE, "SRNL_FLAG_RECORD: params->workspace must hold the forward record");
+        if (!is_device_ptr(p->workspace) || !aligned16(p->workspace))
+            return fail(SRNL_ERR_PTR, "params->workspace must be 16-byte aligned device memory");
+    }
     float *ws = static_cast<float *>(workspace);
     if (p->in_dtype == SRNL_F32)
         return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq, dstates);

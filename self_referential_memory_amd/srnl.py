@@ -24,6 +24,7 @@ FLAG_HARD_CAP, FLAG_NO_CAP, FLAG_NO_CLAMP, FLAG_FIXED_ALPHA, FLAG_READ_BEFORE = 
     0x1, 0x2, 0x4, 0x8, 0x10)
 FLAG_FREEZE_KV = 0x20
 FLAG_CHECK_FINITE = 0x40
+FLAG_RECORD = 0x80
 
 EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
@@ -218,6 +219,33 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
     return out
 
 
+def scan_fwd_record(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
+                    route_mask: int = 15, q: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, *, flags: int = 0, **kw):
+    """srnl_scan_fwd with SRNL_FLAG_RECORD: the route outputs [R,B,H*W,C] and
+    the forward record (a uint8 device tensor, or None where the windowed
+    backward does not apply) for scan_bwd(..., record=...)."""
+    B, H, W, C = x.shape
+    R = bin(route_mask & 15).count("1")
+    _expect(states, _state_shape(heads, d), torch.float32, "states")
+    if out is None:
+        out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
+    _expect(out, (R, B, H * W, C), torch.float32, "out")
+    p = make_params(states, x, q, flags=flags | FLAG_RECORD, **kw)
+    only = Params.from_buffer_copy(p)
+    only.flags &= ~FLAG_CHECK_FINITE
+    rec_bytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask,
+                                                ctypes.byref(only))
+    nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    if ws is not None:
+        p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
+    _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
+                               _ptr(out)), "srnl_scan_fwd")
+    rec = ws[:rec_bytes] if rec_bytes else None
+    return out, rec
+
+
 def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
             q: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, *,
             chunk: int = 0, params: Optional[Params] = None, **kw) -> torch.Tensor:
@@ -254,14 +282,20 @@ def fuse(y: torch.Tensor, B: int, H: int, W: int, C: int, route_mask: int,
 
 def scan_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torch.Tensor,
              route_mask: int = 15, q: Optional[torch.Tensor] = None, *,
-             params: Optional[Params] = None, **kw):
+             params: Optional[Params] = None, record: Optional[torch.Tensor] = None, **kw):
     """srnl_scan_bwd: dy [R,B,H*W,C] fp32 -> (dx [B,H,W,C], dq or None, dstates
-    [4,heads,3d^2+2d]), all fp32. The workspace is allocated here (torch)."""
+    [4,heads,3d^2+2d]), all fp32. The workspace is allocated here (torch).
+    ``record``: the forward record from scan_fwd_record with the same
+    arguments; the backward then reads it instead of recomputing it."""
     B, H, W, C = x.shape
     R = bin(route_mask & 15).count("1")
     _expect(states, _state_shape(heads, d), torch.float32, "states")
     _expect(dy, (R, B, H * W, C), torch.float32, "dy")
     p = params if params is not None else make_params(states, x, q, **kw)
+    if record is not None:
+        p = Params.from_buffer_copy(p)
+        p.flags = (p.flags | FLAG_RECORD) & ~FLAG_CHECK_FINITE
+        p.workspace, p.workspace_bytes = record.data_ptr(), record.numel() * record.element_size()
     nbytes = lib().srnl_scan_bwd_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
     dx = torch.empty((B, H, W, C), dtype=torch.float32, device=x.device)
@@ -330,26 +364,27 @@ class Operator(torch.autograd.Function):
     """The operator (scan + fuse) as an autograd node: the forward pass is
     srnl_scan_fwd and srnl_fuse, the backward pass srnl_fuse_bwd and
     srnl_scan_bwd. Gradients flow to x, the initial states, the scales and
-    the separate queries. The route outputs are kept for the fusion backward;
-    srnl_scan_bwd recomputes everything else from x and the states."""
+    the separate queries. The route outputs are kept for the fusion backward,
+    and, where the windowed backward applies, the forward's record
+    (SRNL_FLAG_RECORD), so the backward does not run the forward again."""
 
     @staticmethod
     def forward(ctx, x, states, scales, q, heads, d, route_mask, kw):
         B, H, W, C = x.shape
-        y = scan_fwd(x, states, heads, d, route_mask, q, **kw)
+        y, rec = scan_fwd_record(x, states, heads, d, route_mask, q, **kw)
         out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype, stream=kw.get("stream"))
-        ctx.save_for_backward(x, states, scales, q, y)
+        ctx.save_for_backward(x, states, scales, q, y, rec)
         ctx.cfg = (heads, d, route_mask, kw)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        x, states, scales, q, y = ctx.saved_tensors
+        x, states, scales, q, y, rec = ctx.saved_tensors
         heads, d, route_mask, kw = ctx.cfg
         B, H, W, C = x.shape
         dout = dout.to(torch.float32).contiguous()
         dyr, dsc = fuse_bwd(dout, y, B, H, W, C, route_mask, scales, stream=kw.get("stream"))
-        dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, **kw)
+        dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, record=rec, **kw)
         return (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype),
                 None, None, None, None)
 

@@ -47,8 +47,16 @@ static void scan_args(void)
     EXPECT(srnl_scan_fwd(NULL, 1, 2, 2, 8, 2, 4, 15, &p, NULL) == SRNL_ERR_PTR);
     p.alpha_max = 1.0f;
     EXPECT(srnl_scan_fwd(NULL, 1, 2, 2, 8, 2, 4, 15, &p, NULL) == SRNL_ERR_ARG);
-    p = params(0x80u);
+    p = params(0x100u);
     EXPECT(srnl_scan_fwd(NULL, 1, 2, 2, 8, 2, 4, 15, &p, NULL) == SRNL_ERR_ARG);
+    p = params(SRNL_FLAG_RECORD);
+    EXPECT(srnl_scan_workspace_bytes(2, 3, 4, 64, 2, 32, 15, &p) > 0);
+    EXPECT(srnl_scan_workspace_bytes(2, 3, 4, 32, 2, 16, 15, &p) == 0);
+    EXPECT(srnl_scan_workspace_bytes(1 << 22, 1 << 15, 1 << 15, 64, 2, 32, 15, &p) == 0);
+    EXPECT(srnl_scan_fwd(NULL, 1 << 22, 1 << 15, 1 << 15, 64, 2, 32, 15, &p, NULL) == SRNL_ERR_ARG);
+    EXPECT(srnl_scan_fwd(NULL, 1, 2, 2, 64, 2, 32, 15, &p, NULL) == SRNL_ERR_PTR);
+    EXPECT(srnl_scan_bwd(NULL, 1, 2, 2, 64, 2, 32, 15, &p, NULL, NULL, 0, NULL, NULL, NULL) !=
+           SRNL_OK);
     p = params(SRNL_FLAG_CHECK_FINITE);
     EXPECT(srnl_scan_fwd(NULL, 1, 2, 2, 8, 2, 4, 15, &p, NULL) == SRNL_ERR_PTR);
     p.in_dtype = (srnl_dtype)7;
@@ -88,6 +96,9 @@ static void other_args(void)
     EXPECT(srnl_scan_bwd_workspace_bytes(1, 4, 4, 60, 2, 32, 15, &p) == 0);
     EXPECT(srnl_scan_bwd_workspace_bytes(1 << 30, 1 << 15, 1 << 15, 64, 1, 64, 15, &p) == 0);
     EXPECT(srnl_scan_bwd_workspace_bytes(1, 4, 4, 64, 2, 32, 15, NULL) == 0);
+    EXPECT(srnl_scan_bwd_workspace_bytes(1 << 22, 1 << 15, 1 << 15, 64, 2, 32, 15, &p) == 0);
+    EXPECT(srnl_scan_bwd(NULL, 1 << 22, 1 << 15, 1 << 15, 64, 2, 32, 15, &p, NULL, NULL, 0, NULL,
+                         NULL, NULL) == SRNL_ERR_ARG);
     EXPECT(srnl_scan_bwd(NULL, 1, 4, 4, 64, 2, 32, 15, NULL, NULL, NULL, 0, NULL, NULL, NULL) ==
            SRNL_ERR_PTR);
     EXPECT(srnl_scan_bwd(NULL, 1, 4, 4, 60, 2, 32, 15, &p, NULL, NULL, 0, NULL, NULL, NULL) ==

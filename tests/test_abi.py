@@ -75,8 +75,8 @@ def _scan(x=0, B=1, H=2, W=2, C=8, heads=2, d=4, mask=15, **kw):
     (dict(eps=0.0), srnl.SRNL_ERR_ARG),
     (dict(eps=float("inf")), srnl.SRNL_ERR_ARG),
     (dict(chunk_row=-1), srnl.SRNL_ERR_ARG),
-    (dict(flags=0x100), srnl.SRNL_ERR_ARG),
-    (dict(flags=0x80), srnl.SRNL_ERR_ARG),          # first bit above the known flags
+    (dict(flags=0x100), srnl.SRNL_ERR_ARG),         # first bit above the known flags
+    (dict(flags=0x200), srnl.SRNL_ERR_ARG),
     (dict(in_dtype=7), srnl.SRNL_ERR_DTYPE),
     (dict(B=1 << 30, H=1 << 15, W=1 << 15, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # overflow
     (dict(B=1, H=1 << 16, W=1 << 16, heads=1, d=64, C=64), srnl.SRNL_ERR_ARG),  # H*W > INT_MAX
@@ -128,6 +128,19 @@ def test_scan_workspace_bytes():
     assert ws(srnl.FLAG_CHECK_FINITE, B=0) == 0     # empty grid
     assert ws(srnl.FLAG_CHECK_FINITE, C=12) == 0    # invalid shape
     assert L.srnl_scan_workspace_bytes(1, 2, 2, 8, 2, 4, 15, None) == 0
+    # the forward record: only where the windowed backward applies (d = 32,
+    # readout after the write), 256-byte aligned, counters after it
+    rec = ws(srnl.FLAG_RECORD, C=64, heads=2, d=32)
+    assert rec > 0 and rec % 256 == 0
+    assert ws(srnl.FLAG_RECORD | srnl.FLAG_CHECK_FINITE, C=64, heads=2, d=32) == rec + 256
+    assert ws(srnl.FLAG_RECORD | srnl.FLAG_READ_BEFORE, C=64, heads=2, d=32) == 0
+    assert ws(srnl.FLAG_RECORD, C=32, heads=2, d=16) == 0
+    # with the record given, the backward's own workspace is smaller
+    p0 = srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, 0, None)
+    p1 = srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, srnl.FLAG_RECORD, None)
+    b0 = L.srnl_scan_bwd_workspace_bytes(2, 3, 4, 64, 2, 32, 15, ctypes.byref(p0))
+    b1 = L.srnl_scan_bwd_workspace_bytes(2, 3, 4, 64, 2, 32, 15, ctypes.byref(p1))
+    assert 0 < b1 < b0 and b0 - b1 <= rec
     # an empty grid is a no-op with the check as without it
     assert _scan(B=0, flags=srnl.FLAG_CHECK_FINITE) == srnl.SRNL_OK
 

@@ -281,3 +281,74 @@ def test_backward_on_a_side_stream_matches():
     torch.cuda.synchronize()
     assert torch.equal(dy, ref_dy) and torch.equal(dsc, ref_dsc)
     assert torch.equal(got[0], ref[0]) and torch.equal(got[2], ref[2])
+
+
+@pytest.mark.parametrize("case", ["hier", "long_q_f32", "ragged_q_f32", "short_chunks", "t32",
+                                  "variants", "fixed_alpha"])
+def test_forward_record_matches(case):
+    """SRNL_FLAG_RECORD: the forward that keeps its record gives the plain
+    forward's outputs bitwise, and the backward that reads that record gives
+    bitwise the gradients of the backward that records by itself."""
+    flags = 0
+    if case == "hier":
+        wl = _wl("rec_h", 2, 56, 56, 2, 32, dtype="bf16", seed=21)
+    elif case == "long_q_f32":
+        wl = _wl("rec_l", 2, 40, 40, 2, 32, dtype="f32", seed=29, separate_q=True)
+    elif case == "ragged_q_f32":
+        wl = _wl("rec_q", 2, 9, 13, 2, 32, dtype="f32", seed=22, separate_q=True,
+                 chunk_row=5, chunk_col=4)
+    elif case == "short_chunks":
+        wl = _wl("rec_s", 3, 7, 7, 2, 32, dtype="bf16", seed=23)
+    elif case == "t32":
+        wl = _wl("rec_t", 2, 28, 20, 2, 32, dtype="bf16", seed=24)
+    elif case == "variants":
+        wl = _wl("rec_v", 2, 12, 17, 2, 32, dtype="f32", seed=25, state_std=2.0,
+                 outlier_frac=0.05)
+        flags = srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP | srnl.FLAG_FREEZE_KV
+    else:
+        wl = _wl("rec_a", 2, 10, 11, 2, 32, dtype="bf16", seed=26)
+        flags = srnl.FLAG_FIXED_ALPHA
+    print(f"[gpu] record {case} {wl.B}x{wl.H}x{wl.W} flags={flags}", flush=True)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(wl.x).to(DEV).to(dt)
+    q = None if wl.q is None else torch.from_numpy(wl.q).to(DEV).to(dt)
+    st = torch.from_numpy(wl.states).to(DEV)
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps, chunk_row=wl.chunk_row,
+              chunk_col=wl.chunk_col, flags=flags)
+    y0 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15, q, **kw)
+    y1, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15, q, **kw)
+    assert rec is not None
+    dy = torch.from_numpy(np.random.default_rng(7).standard_normal(tuple(y0.shape))
+                          .astype(np.float32)).to(DEV)
+    g0 = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15, q, **kw)
+    g1 = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15, q, record=rec, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for a, b in zip(g0, g1):
+        assert (a is None and b is None) or torch.equal(a, b)
+
+
+def test_forward_record_where_it_does_not_apply_and_errors():
+    """d = 16 and the readout-before-write variant have no record: the
+    forward runs plainly and the binding returns None. A record smaller than
+    the sizes need is a workspace error in both directions."""
+    print("[gpu] record n/a and errors", flush=True)
+    wl = _wl("rec_n", 2, 5, 6, 2, 16, dtype="f32", seed=27)
+    x = torch.from_numpy(wl.x).to(DEV)
+    st = torch.from_numpy(wl.states).to(DEV)
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15)
+    assert rec is None and torch.equal(y, srnl.scan_fwd(x, st, wl.heads, wl.d, 15))
+    wl = _wl("rec_e", 2, 5, 6, 2, 32, dtype="f32", seed=28)
+    x = torch.from_numpy(wl.x).to(DEV)
+    st = torch.from_numpy(wl.states).to(DEV)
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15, flags=srnl.FLAG_READ_BEFORE)
+    assert rec is None
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15)
+    p = srnl.make_params(st, x, flags=srnl.FLAG_RECORD)
+    p.workspace, p.workspace_bytes = rec.data_ptr(), rec.numel() - 256
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd(x, st, wl.heads, wl.d, 15, params=p)
+    assert e.value.status == srnl.SRNL_ERR_WORKSPACE
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_bwd(x, st, wl.heads, wl.d, torch.zeros_like(y), 15, record=rec[:-256])
+    assert e.value.status == srnl.SRNL_ERR_WORKSPACE
