@@ -84,13 +84,16 @@ typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
  * stream to finish. Other entry points ignore the flag. */
 #define SRNL_FLAG_CHECK_FINITE 0x40u
 /* Keep the forward's record for the backward pass (training). srnl_scan_fwd
- * also writes, into params->workspace, the per-chain record that the
+ * (and srnl_scan_1d, the scan of a 1 x N grid, whose backward is
+ * srnl_scan_bwd on that grid with SRNL_ROUTE_ROW) also writes, into
+ * params->workspace, the per-chain record that the
  * windowed backward reads (each chunk's boundary rows and closing Q, and each
  * 16-token window's opening Q, u rows and transition scalars); srnl_scan_bwd
  * called with the same arguments, flags and workspace then reads that record
  * instead of recomputing it. Applies where the windowed backward does: d = 32
  * with the readout after the write; elsewhere, and in the other entry points,
- * the flag changes nothing. The record takes srnl_scan_workspace_bytes. */
+ * the flag changes nothing. The record takes srnl_scan_workspace_bytes (for
+ * srnl_scan_1d, of the 1 x N grid). */
 #define SRNL_FLAG_RECORD 0x80u
 
 /* Floats of initial state per (route, head): 3d^2 + 2d. */
