@@ -1229,6 +1229,11 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     parity: one barrier per window); Z is left as two partial sums
         //     (each wave also takes half of the N U terms) that the readout adds.
         if (wave < CW) {
+            // the window chain is the chunk's critical path: with the long
+            // sub-blocks (two chains a CU) its waves issue ahead of the
+            // other chain's
+            if constexpr (T >= 64)
+                __builtin_amdgcn_s_setprio(2);
             const int it = wave % NTC, jg = wave / NTC;
             float4 kv[NJ], qv[NJ];
             auto load_rows = [&](int tb) {
@@ -1324,6 +1329,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 for (int i = 0; i < 4; ++i)
                     zd[ix(tb + 4 * lk + i, 16 * it + lm)] = Z[i];
             }
+            if constexpr (T >= 64)
+                __builtin_amdgcn_s_setprio(0);
             if constexpr (QT_EARLY) {
                 if (chunk_end && cend < N)
                     stage_qt();
