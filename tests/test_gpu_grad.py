@@ -352,3 +352,28 @@ def test_forward_record_where_it_does_not_apply_and_errors():
     with pytest.raises(srnl.SrnlError) as e:
         srnl.scan_bwd(x, st, wl.heads, wl.d, torch.zeros_like(y), 15, record=rec[:-256])
     assert e.value.status == srnl.SRNL_ERR_WORKSPACE
+
+
+def test_forward_record_with_finite_check():
+    """SRNL_FLAG_RECORD with SRNL_FLAG_CHECK_FINITE: the counters sit after
+    the record in the one workspace; the record still serves the backward,
+    and a NaN input is still reported."""
+    print("[gpu] record + finite check", flush=True)
+    wl = _wl("rec_f", 2, 9, 10, 2, 32, dtype="bf16", seed=30)
+    x = torch.from_numpy(wl.x).to(DEV).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(DEV)
+    y0 = srnl.scan_fwd(x, st, wl.heads, wl.d, 15)
+    y1, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15, flags=srnl.FLAG_CHECK_FINITE)
+    dy = torch.from_numpy(np.random.default_rng(8).standard_normal(tuple(y0.shape))
+                          .astype(np.float32)).to(DEV)
+    g0 = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15)
+    g1 = srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15, record=rec)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert torch.equal(g0[0], g1[0]) and torch.equal(g0[2], g1[2])
+    xb = x.clone()
+    xb.view(-1)[3] = float("nan")
+    with pytest.raises(srnl.SrnlError) as e:
+        srnl.scan_fwd_record(xb, st, wl.heads, wl.d, 15, flags=srnl.FLAG_CHECK_FINITE)
+    assert e.value.status == srnl.SRNL_ERR_NONFINITE
+    assert "1 non-finite input values" in str(e.value)
