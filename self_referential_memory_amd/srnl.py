@@ -186,12 +186,18 @@ def make_params(states: torch.Tensor, x: torch.Tensor, q: Optional[torch.Tensor]
 def _finite_check_workspace(p: Params, x: torch.Tensor, B, H, W, C, heads, d, route_mask):
     """With SRNL_FLAG_CHECK_FINITE and no caller workspace, allocate one and
     point p at it; the call waits for its stream when checking, so the buffer
-    outlives its use. Returns the tensor (None when nothing was allocated)."""
-    if not (p.flags & FLAG_CHECK_FINITE) or p.workspace:
+    outlives its use. Returns the tensor (None when nothing was allocated).
+    A record (SRNL_FLAG_RECORD) must outlive the call: that takes
+    scan_fwd_record or a caller workspace."""
+    if p.workspace:
         return None
     nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
     if not nbytes:
         return None
+    if p.flags & FLAG_RECORD and nbytes > (256 if p.flags & FLAG_CHECK_FINITE else 0):
+        raise ValueError("FLAG_RECORD needs a workspace that outlives the call: use "
+                         "scan_fwd_record, which returns the record, or pass params "
+                         "with a workspace")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
     return ws
