@@ -18,17 +18,24 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "srnl_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libsrnl_oracle.so")
+# The same source built with every state, product and sum in IEEE single
+# precision. Not a reference: it measures how far an fp32 evaluation of the
+# recurrence can drift from the double result on a given input (the
+# conditioning of each chunk), which sets the per-chunk parity bar.
+LIB32_PATH = os.path.join(_HERE, "libsrnl_oracle_f32.so")
 
 CAP_SOFT, CAP_HARD, CAP_OFF = 0, 1, 2
 TRACE_W = 18
 
 
 def build() -> str:
-    """Compile the oracle with plain gcc (IEEE double, no fast-math)."""
-    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", LIB_PATH + ".tmp", _SRC, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    """Compile the oracle with plain gcc (IEEE double, no fast-math, no
+    contraction of products into fused multiply-adds), and its fp32 build."""
+    for path, extra in ((LIB_PATH, []), (LIB32_PATH, ["-DSRNL_ORACLE_REAL=float"])):
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall",
+               "-Wextra"] + extra + ["-o", path + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(path + ".tmp", path)
     return LIB_PATH
 
 
@@ -41,16 +48,18 @@ class _Opts(ctypes.Structure):
                 ("freeze_kv", ctypes.c_int)]
 
 
-_lib = None
+_libs = {}
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH) or (
-                os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
+def lib(precision: str = "f64"):
+    """The oracle library: "f64" (the reference) or "f32" (conditioning
+    measurements only)."""
+    if precision not in _libs:
+        path = {"f64": LIB_PATH, "f32": LIB32_PATH}[precision]
+        if any(not os.path.exists(p) or os.path.getmtime(p) < os.path.getmtime(_SRC)
+               for p in (LIB_PATH, LIB32_PATH)):
             build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         L.srnl_oracle_scan.argtypes = [dp, dp] + [ctypes.c_int] * 6 + [
             ctypes.c_uint, dp, ctypes.POINTER(_Opts), dp, dp]
@@ -64,8 +73,8 @@ def lib():
         L.srnl_oracle_route_index.restype = None
         L.srnl_oracle_chunk_len.argtypes = [ctypes.c_int] * 5
         L.srnl_oracle_chunk_len.restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _libs[precision] = L
+    return _libs[precision]
 
 
 def _p(a: Optional[np.ndarray]):
@@ -73,6 +82,18 @@ def _p(a: Optional[np.ndarray]):
         return None
     assert a.dtype == np.float64 and a.flags.c_contiguous
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def perturbed(a, k: int):
+    """a (None allowed) with every element multiplied by 1 +- 2^-24, the fp32
+    rounding unit, with signs drawn from numpy's seeded generator (seed
+    1000 + k), in float64. The fp32 build run on such copies gives further
+    fp32 evaluations of a problem that fp32 cannot tell from the original:
+    their spread on a chunk measures that chunk's conditioning."""
+    if a is None:
+        return None
+    rng = np.random.default_rng(1000 + k)
+    return np.asarray(a, np.float64) * (1.0 + 2.0 ** -24 * rng.choice([-1.0, 1.0], np.shape(a)))
 
 
 def route_index(r: int, H: int, W: int, t: int):
@@ -89,12 +110,14 @@ def scan(x, states, heads: int, d: int, route_mask: int = 15, q=None, *,
          alpha_max: float = 0.9, eps: float = 1e-6, chunk_row: int = 0,
          chunk_col: int = 0, cap_mode: int = CAP_SOFT, clamp: bool = True,
          fixed_alpha: bool = False, readout_before: bool = False,
-         freeze_kv: bool = False, trace: bool = False, threads: int = 1):
+         freeze_kv: bool = False, trace: bool = False, threads: int = 1,
+         precision: str = "f64"):
     """Per-route outputs y [R][B][H*W][C] (traversal order) in float64.
 
     ``threads`` > 1 splits the batch over Python threads (each runs the
     single-threaded oracle on its own slice; ctypes releases the GIL).
-    Returns y, or (y, trace) when ``trace`` is set."""
+    ``precision="f32"`` runs the fp32 build (conditioning measurements, not a
+    reference). Returns y, or (y, trace) when ``trace`` is set."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     B, H, W, C = x.shape
     st = np.ascontiguousarray(states, dtype=np.float64)
@@ -109,7 +132,7 @@ def scan(x, states, heads: int, d: int, route_mask: int = 15, q=None, *,
         qs = None if qq is None else np.ascontiguousarray(qq[b0:b1])
         ys = np.zeros((R, b1 - b0, N, C))
         tr = np.zeros((R, b1 - b0, heads, N, TRACE_W)) if trace else None
-        rc = lib().srnl_oracle_scan(_p(xs), _p(qs), b1 - b0, H, W, C, heads, d,
+        rc = lib(precision).srnl_oracle_scan(_p(xs), _p(qs), b1 - b0, H, W, C, heads, d,
                                     route_mask, _p(st), ctypes.byref(opts),
                                     _p(ys), _p(tr))
         if rc != 0:

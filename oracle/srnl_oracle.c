@@ -76,6 +76,14 @@
  * write (alternative readings). With the memories frozen only the content
  * memory M_c is written; M_k, M_v, m_eta and m_alpha keep their initial
  * values for the whole scan, so every chunk generates from them.  (READING)
+ *
+ * Precision. The reference is this file built as is: every state, product
+ * and sum in IEEE double. Built with -DSRNL_ORACLE_REAL=float, the same
+ * steps keep their states, products and sums in IEEE single precision
+ * (inputs rounded to float when read, libm results rounded to float). That
+ * second build is no reference: the tests use it only to measure how far any
+ * evaluation in fp32 can drift from the double result on a given chunk of
+ * a given input (the conditioning of that chunk).
  */
 #include <math.h>
 #include <stddef.h>
@@ -83,6 +91,11 @@
 #include <string.h>
 
 #include "srnl_oracle.h"
+
+#ifndef SRNL_ORACLE_REAL
+#define SRNL_ORACLE_REAL double
+#endif
+typedef SRNL_ORACLE_REAL real;
 
 /* Route traversal: token t of route r visits grid cell (i, j). */
 void srnl_oracle_route_index(int r, int H, int W, long t, int *i, int *j)
@@ -107,11 +120,11 @@ int srnl_oracle_chunk_len(int r, int H, int W, int chunk_row, int chunk_col)
     return chunk_col > 0 ? chunk_col : H;
 }
 
-static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+static real sigmoid(real z) { return (real)1 / ((real)1 + (real)exp(-z)); }
 
-static double dot(const double *a, const double *b, int n)
+static real dot(const real *a, const real *b, int n)
 {
-    double s = 0.0;
+    real s = 0;
     for (int j = 0; j < n; ++j)
         s += a[j] * b[j];
     return s;
@@ -119,57 +132,58 @@ static double dot(const double *a, const double *b, int n)
 
 /* Per-token quantities produced from the boundary states. */
 typedef struct {
-    double *khat;   /* d */
-    double *e;      /* d: khat - v */
-    double *w;      /* 3d+2: boundary rows applied to e */
-    double alpha, eta, eta1, eta2, g, nkh;
+    real *khat;   /* d */
+    real *e;      /* d: khat - v */
+    real *w;      /* 3d+2: boundary rows applied to e */
+    real alpha, eta, eta1, eta2, g, nkh;
 } token_gen;
 
 /* Boundary generation for one token (any order inside a chunk). `bnd` holds
  * the 3d+2 boundary rows: rows [0,d) M_c, [d,2d) M_k, [2d,3d) M_v, 3d m_eta,
  * 3d+1 m_alpha. */
-static void generate(const double *bnd, int d, const double *xt,
-                     const srnl_oracle_opts *o, token_gen *g, double *scratch)
+static void generate(const real *bnd, int d, const real *xt,
+                     const srnl_oracle_opts *o, token_gen *g, real *scratch)
 {
-    const double *Bk = bnd + (size_t)d * d;
-    const double *Bv = bnd + (size_t)2 * d * d;
-    const double *beta = bnd + (size_t)3 * d * d;
-    const double *balpha = beta + d;
-    double *k = scratch, *v = scratch + d;
+    const real *Bk = bnd + (size_t)d * d;
+    const real *Bv = bnd + (size_t)2 * d * d;
+    const real *beta = bnd + (size_t)3 * d * d;
+    const real *balpha = beta + d;
+    real *k = scratch, *v = scratch + d;
     int rows = 3 * d + 2;
+    const real alpha_max = (real)o->alpha_max, eps = (real)o->eps;
 
     for (int i = 0; i < d; ++i) {
         k[i] = dot(Bk + (size_t)i * d, xt, d);   /* key memory generates k */
         v[i] = dot(Bv + (size_t)i * d, xt, d);   /* value memory generates v */
     }
     g->eta = sigmoid(dot(beta, xt, d));          /* learning-rate memory */
-    g->alpha = o->fixed_alpha ? o->alpha_max
-                              : o->alpha_max * sigmoid(dot(balpha, xt, d));
+    g->alpha = o->fixed_alpha ? alpha_max
+                              : alpha_max * sigmoid(dot(balpha, xt, d));
 
-    double nk2 = dot(k, k, d);
-    double inv = 1.0 / sqrt(nk2 + o->eps);       /* stabilised L2 norm */
+    real nk2 = dot(k, k, d);
+    real inv = (real)1 / (real)sqrt(nk2 + eps);  /* stabilised L2 norm */
     for (int i = 0; i < d; ++i)
         g->khat[i] = k[i] * inv;
     for (int i = 0; i < d; ++i)
         g->e[i] = g->khat[i] - v[i];             /* key-value discrepancy */
 
-    double nkh2 = dot(g->khat, g->khat, d);
-    g->nkh = sqrt(nkh2);
-    g->g = sqrt(dot(g->e, g->e, d)) * g->nkh;
+    real nkh2 = dot(g->khat, g->khat, d);
+    g->nkh = (real)sqrt(nkh2);
+    g->g = (real)sqrt(dot(g->e, g->e, d)) * g->nkh;
 
     /* injection cap: keep eta' * g inside the margin 1 - alpha */
-    double m = 1.0 - g->alpha;
+    real m = (real)1 - g->alpha;
     if (o->cap_mode == SRNL_ORACLE_CAP_SOFT) {
-        g->eta1 = (g->g > 0.0) ? m * tanh(g->eta * g->g / m) / g->g : g->eta;
+        g->eta1 = (g->g > 0) ? m * (real)tanh(g->eta * g->g / m) / g->g : g->eta;
     } else if (o->cap_mode == SRNL_ORACLE_CAP_HARD) {
-        g->eta1 = (g->g > 0.0 && m / g->g < g->eta) ? m / g->g : g->eta;
+        g->eta1 = (g->g > 0 && m / g->g < g->eta) ? m / g->g : g->eta;
     } else {
         g->eta1 = g->eta;
     }
     /* spectral clamp: |alpha - eta'' |k^|^2| <= alpha */
     g->eta2 = g->eta1;
-    if (o->clamp && nkh2 > 0.0) {
-        double cap = 2.0 * g->alpha / nkh2;
+    if (o->clamp && nkh2 > 0) {
+        real cap = (real)2 * g->alpha / nkh2;
         if (cap < g->eta2)
             g->eta2 = cap;
     }
@@ -180,18 +194,31 @@ static void generate(const double *bnd, int d, const double *xt,
 
 /* One retained-DGD step on the working rows: all 3d+2, or only the d rows
  * of M_c when the other memories are frozen. */
-static void write_token(double *mem, int d, const token_gen *g, int freeze_kv)
+static void write_token(real *mem, int d, const token_gen *g, int freeze_kv)
 {
     int rows = freeze_kv ? d : 3 * d + 2;
     for (int r = 0; r < rows; ++r) {
-        double *m = mem + (size_t)r * d;
-        double s = dot(m, g->khat, d) + g->w[r];  /* M k^ + B e */
+        real *m = mem + (size_t)r * d;
+        real s = dot(m, g->khat, d) + g->w[r];    /* M k^ + B e */
         for (int j = 0; j < d; ++j)
             m[j] = g->alpha * m[j] - g->eta2 * s * g->khat[j];
     }
 }
 
-static double frob(const double *a, int n) { return sqrt(dot(a, a, n)); }
+static double frob(const real *a, int n)
+{
+    double s = 0.0;
+    for (int j = 0; j < n; ++j)
+        s += (double)a[j] * a[j];
+    return sqrt(s);
+}
+
+/* d consecutive input values, rounded to the working precision */
+static void read_row(real *dst, const double *src, int d)
+{
+    for (int a = 0; a < d; ++a)
+        dst[a] = (real)src[a];
+}
 
 int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
                      int C, int heads, int d, unsigned route_mask,
@@ -207,16 +234,16 @@ int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
     const long N = (long)H * W;
     const int rows = 3 * d + 2;
     const size_t ssz = (size_t)rows * d;
-    double *mem = malloc(ssz * sizeof(double));
-    double *bnd = malloc(ssz * sizeof(double));
-    double *scratch = malloc(2 * (size_t)d * sizeof(double));
-    double *xt = malloc((size_t)d * sizeof(double));
-    double *qt = malloc((size_t)d * sizeof(double));
+    real *mem = malloc(ssz * sizeof(real));
+    real *bnd = malloc(ssz * sizeof(real));
+    real *scratch = malloc(2 * (size_t)d * sizeof(real));
+    real *xt = malloc((size_t)d * sizeof(real));
+    real *qt = malloc((size_t)d * sizeof(real));
     int Lmax = W > H ? W : H;
     if (o->chunk_row > Lmax) Lmax = o->chunk_row;
     if (o->chunk_col > Lmax) Lmax = o->chunk_col;
     if (Lmax > N) Lmax = (int)N;
-    double *genbuf = malloc((size_t)Lmax * (2 * d + rows) * sizeof(double));
+    real *genbuf = malloc((size_t)Lmax * (2 * d + rows) * sizeof(real));
     token_gen *gen = malloc((size_t)Lmax * sizeof(token_gen));
     if (!mem || !bnd || !scratch || !xt || !qt || !genbuf || !gen) {
         free(mem); free(bnd); free(scratch); free(xt); free(qt);
@@ -224,7 +251,7 @@ int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
         return -2;
     }
     for (int t = 0; t < Lmax; ++t) {
-        double *base = genbuf + (size_t)t * (2 * d + rows);
+        real *base = genbuf + (size_t)t * (2 * d + rows);
         gen[t].khat = base;
         gen[t].e = base + d;
         gen[t].w = base + 2 * d;
@@ -238,24 +265,22 @@ int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
         for (int b = 0; b < B; ++b) {
             for (int h = 0; h < heads; ++h) {
                 /* a fresh trajectory from this route's learned states */
-                memcpy(mem, states + ((size_t)r * heads + h) * ssz,
-                       ssz * sizeof(double));
+                read_row(mem, states + ((size_t)r * heads + h) * ssz, (int)ssz);
                 for (long c0 = 0; c0 < N; c0 += L) {
                     long nc = (N - c0 < L) ? (N - c0) : L;
-                    memcpy(bnd, mem, ssz * sizeof(double)); /* boundary */
+                    memcpy(bnd, mem, ssz * sizeof(real)); /* boundary */
                     for (long u = 0; u < nc; ++u) {
                         int i, j;
                         srnl_oracle_route_index(r, H, W, c0 + u, &i, &j);
-                        const double *px = x + (((size_t)b * H + i) * W + j) * C + (size_t)h * d;
-                        generate(bnd, d, px, o, &gen[u], scratch);
+                        read_row(xt, x + (((size_t)b * H + i) * W + j) * C + (size_t)h * d, d);
+                        generate(bnd, d, xt, o, &gen[u], scratch);
                     }
                     for (long u = 0; u < nc; ++u) {
                         long t = c0 + u;
                         int i, j;
                         srnl_oracle_route_index(r, H, W, t, &i, &j);
                         const double *src = q ? q : x;
-                        memcpy(qt, src + (((size_t)b * H + i) * W + j) * C + (size_t)h * d,
-                               (size_t)d * sizeof(double));
+                        read_row(qt, src + (((size_t)b * H + i) * W + j) * C + (size_t)h * d, d);
                         double *yt = y + (((size_t)slot * B + b) * N + t) * C + (size_t)h * d;
                         if (o->readout_before)
                             for (int a = 0; a < d; ++a)
@@ -280,7 +305,7 @@ int srnl_oracle_scan(const double *x, const double *q, int B, int H, int W,
                             tr[13] = g->eta2;
                             tr[14] = g->g;
                             tr[15] = g->nkh;
-                            tr[16] = fabs(g->alpha - g->eta2 * g->nkh * g->nkh);
+                            tr[16] = fabs((double)(g->alpha - g->eta2 * g->nkh * g->nkh));
                             tr[17] = (double)u;
                         }
                     }

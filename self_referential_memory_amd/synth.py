@@ -294,6 +294,14 @@ def hier56(B: int = 64) -> Workload:
     return make("hier56", B, 56, 56, 64, 2, 32, "bf16", 2, x_kind="ar1", rho=0.9)
 
 
+def hier56_live(B: int = 64) -> Workload:
+    """hier56's launch shape and input (AR(1) rows, seed 2) on states of std 1
+    with retention fixed at alpha_max = 0.999 (run with the fixed-retention
+    flag): the memories stay O(1) over all 56 chunks of every route."""
+    return make("hier56_live", B, 56, 56, 64, 2, 32, "bf16", 2, x_kind="ar1", rho=0.9,
+                state_std=1.0, alpha_max=0.999)
+
+
 def hier_sweep(B: int = 64) -> List[Workload]:
     stages = [(56, 64, 2), (28, 128, 4), (14, 256, 8), (7, 512, 16)]
     return [make(f"hier_sweep_{s}x{s}", B, s, s, C, h, 32, "bf16", 3)

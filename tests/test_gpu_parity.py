@@ -6,20 +6,30 @@ and for the fused output):
   * fp32 per-route scan outputs: 1e-4, for fp32 and for bf16 inputs (both
     sides read the same bf16 bytes, so only fp32 arithmetic separates them);
   * fused output in fp32: 1e-4; fused output stored as bf16: 2e-2;
-  * additionally, per chunk, max |gpu - oracle| <= 1e-3 * max |oracle| over
-    that chunk's tokens, on every chunk whose output is above 1e-20, so that
-    the late chunks of long scans (where the untrained memories have
-    contracted by many orders of magnitude) are checked on their own scale.
-    The per-chunk bar is wider than the global one because single chunks can
-    be ill-conditioned: an fp32 evaluation of the same recurrence in numpy
-    reaches 4.3e-4 on a chunk of the dense 200x304 map, 3.6e-4 on the
-    adversarial inputs and 1.3e-4 on a d=64 case, matching the GPU;
+  * additionally, per chunk and batch item, on that chunk's own output scale:
+    max |gpu - oracle| <= max(1e-4, 10 e32), where e32 is the largest error
+    (same measure) of four fp32 evaluations of that chunk: the oracle's fp32
+    build (every state, product and sum in IEEE single precision) on the
+    given inputs, and on three copies of the inputs and states whose elements
+    are multiplied by 1 +- 2^-24 (seeded random signs). This checks the late
+    chunks of long scans, where the untrained memories have contracted by
+    many orders of magnitude, on their own scale. Single chunks can be so
+    ill-conditioned that no fp32 evaluation meets 1e-4 on them (the fp32 build
+    reaches 4.5e-4 on a chunk of the adversarial inputs and 2.3e-3 on one of a
+    56x56 grid with states of std 0.5, and one fp32 evaluation alone can be
+    20x luckier than another on the same chunk; tests/test_oracle_fp32.py
+    pins this); the bar follows that measured conditioning, chunk by chunk, and is
+    1e-4 wherever fp32 evaluation is accurate to 1e-5. Chunks whose
+    double-precision output is below 1e-20 are left out (fp32 underflows
+    there);
   * route gather/restore indexing: bit-exact.
-Full-size workloads run on the GPU in full; the oracle checks sampled batch
-items (chains are independent across the batch, so a sample is exact).
+Full-size workloads run on the GPU in full; the oracle checks every batch
+item of the five workloads and sampled items of the larger launches (chains
+are independent across the batch, so a sample is exact).
 """
 import ctypes
 import itertools
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -32,9 +42,11 @@ from self_referential_memory_amd import srnl, synth
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL32 = 1e-4
-TOL_CHUNK = 1e-3
+CHUNK_FACTOR = 10.0
+FP32_REALISATIONS = 4
 TOL_BF16_OUT = 2e-2
 CHUNK_FLOOR = 1e-20
+THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
 def _dev(a, dtype):
@@ -62,8 +74,11 @@ def gpu_forward(wl, route_mask=None, flags=0, out_dtype=None):
 _CAP = {0: oracle.CAP_SOFT, srnl.FLAG_HARD_CAP: oracle.CAP_HARD, srnl.FLAG_NO_CAP: oracle.CAP_OFF}
 
 
-def oracle_forward(wl, bs=None, route_mask=None, flags=0, threads=8):
-    """Oracle on batch items `bs` (all if None), one thread per (b, route)."""
+def oracle_forward(wl, bs=None, route_mask=None, flags=0, threads=THREADS, fp32=False):
+    """Oracle on batch items `bs` (all if None), one thread per (b, route).
+    With fp32, also FP32_REALISATIONS fp32 evaluations of the same items (the
+    fp32 build on the inputs and on perturbed copies: the conditioning of each
+    chunk): returns y, fused, [y32, ...]."""
     rm = wl.route_mask if route_mask is None else route_mask
     bs = list(range(wl.B)) if bs is None else list(bs)
     routes = [r for r in range(4) if (rm >> r) & 1]
@@ -73,20 +88,30 @@ def oracle_forward(wl, bs=None, route_mask=None, flags=0, threads=8):
               fixed_alpha=bool(flags & srnl.FLAG_FIXED_ALPHA),
               readout_before=bool(flags & srnl.FLAG_READ_BEFORE),
               freeze_kv=bool(flags & srnl.FLAG_FREEZE_KV))
+    inputs = {"f64": (wl.x, wl.q, wl.states)}
+    if fp32:
+        inputs[0] = (wl.x, wl.q, wl.states)
+        for k in range(1, FP32_REALISATIONS):
+            inputs[k] = (oracle.perturbed(wl.x, 3 * k), oracle.perturbed(wl.q, 3 * k + 1),
+                         oracle.perturbed(wl.states, 3 * k + 2))
 
-    def job(br):
-        b, r = br
-        q = None if wl.q is None else wl.q[b:b + 1]
-        return oracle.scan(wl.x[b:b + 1], wl.states, wl.heads, wl.d, 1 << r, q, **kw)[0, 0]
+    def job(brk):
+        b, r, key = brk
+        x, q, st = inputs[key]
+        qb = None if q is None else q[b:b + 1]
+        return oracle.scan(x[b:b + 1], st, wl.heads, wl.d, 1 << r, qb,
+                           precision="f64" if key == "f64" else "f32", **kw)[0, 0]
 
-    jobs = list(itertools.product(bs, routes))
+    jobs = list(itertools.product(bs, routes, list(inputs)))
     with ThreadPoolExecutor(max(1, min(threads, len(jobs)))) as ex:
         res = list(ex.map(job, jobs))
-    y = np.zeros((len(routes), len(bs), wl.N, wl.C))
-    for (b, r), yr in zip(jobs, res):
-        y[routes.index(r), bs.index(b)] = yr
-    fused = oracle.fuse(y, len(bs), wl.H, wl.W, wl.C, rm, wl.scales)
-    return y, fused
+    ys = {k: np.zeros((len(routes), len(bs), wl.N, wl.C)) for k in inputs}
+    for (b, r, key), yr in zip(jobs, res):
+        ys[key][routes.index(r), bs.index(b)] = yr
+    fused = oracle.fuse(ys["f64"], len(bs), wl.H, wl.W, wl.C, rm, wl.scales)
+    if fp32:
+        return ys["f64"], fused, [ys[k] for k in range(FP32_REALISATIONS)]
+    return ys["f64"], fused
 
 
 def rel(g, o):
@@ -94,23 +119,39 @@ def rel(g, o):
     return np.abs(g - o).max() / m if m > 0 else np.abs(g).max()
 
 
-def chunk_rel(g, o, L):
-    """Worst per-chunk error relative to that chunk's own output scale, over
-    chunks (per batch item) whose output exceeds CHUNK_FLOOR. g, o: [B,N,C]."""
+def chunk_errors(g, o, L):
+    """Per (chunk, batch item): max |g - o| over the chunk's tokens relative to
+    max |o| there, and max |o|. g, o: [B,N,C]; returns two [chunks, B] arrays."""
     N = o.shape[1]
-    worst = 0.0
+    errs, scales = [], []
     for c0 in range(0, N, L):
         m = np.abs(o[:, c0:c0 + L]).max(axis=(1, 2))
         e = np.abs(g[:, c0:c0 + L] - o[:, c0:c0 + L]).max(axis=(1, 2))
-        live = m > CHUNK_FLOOR
-        if live.any():
-            worst = max(worst, float((e[live] / m[live]).max()))
-    return worst
+        scales.append(m)
+        errs.append(np.where(m > 0, e / np.where(m > 0, m, 1.0), e))
+    return np.array(errs), np.array(scales)
 
 
-def check(wl, bs=None, route_mask=None, flags=0, out_dtype=None, chunk_tol=TOL_CHUNK):
+def check_chunks(g, o, reals, L, what):
+    """Every chunk above CHUNK_FLOOR within max(TOL32, CHUNK_FACTOR e32) of the
+    oracle, e32 being the largest error of the fp32 evaluations `reals` on the
+    same chunk. Returns the number of chunks checked."""
+    eg, m = chunk_errors(g, o, L)
+    e32 = np.max([chunk_errors(y, o, L)[0] for y in reals], axis=0)
+    live = m > CHUNK_FLOOR
+    bar = np.maximum(TOL32, CHUNK_FACTOR * e32)
+    bad = live & (eg > bar)
+    if bad.any():
+        c, b = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: chunk {c} of item {b}: error {eg[c, b]:.3e} > bar "
+                             f"{bar[c, b]:.3e} (fp32 build {e32[c, b]:.3e}); "
+                             f"{int(bad.sum())} chunks over")
+    return int(live.sum())
+
+
+def check(wl, bs=None, route_mask=None, flags=0, out_dtype=None):
     yg, fg = gpu_forward(wl, route_mask, flags, out_dtype)
-    yo, fo = oracle_forward(wl, bs, route_mask, flags)
+    yo, fo, y32 = oracle_forward(wl, bs, route_mask, flags, fp32=True)
     if bs is not None:
         yg, fg = yg[:, list(bs)], fg[list(bs)]
     assert np.isfinite(yg).all()
@@ -120,8 +161,7 @@ def check(wl, bs=None, route_mask=None, flags=0, out_dtype=None, chunk_tol=TOL_C
         e = rel(yg[s], yo[s])
         assert e <= TOL32, (wl.name, "slot", s, e)
         L = min(oracle.chunk_len(r, wl.H, wl.W, wl.chunk_row, wl.chunk_col), wl.N)
-        ec = chunk_rel(yg[s], yo[s], L)
-        assert ec <= chunk_tol, (wl.name, "slot", s, "per-chunk", ec)
+        check_chunks(yg[s], yo[s], [y[s] for y in y32], L, f"{wl.name} slot {s}")
     bf = (wl.dtype == "bf16") if out_dtype is None else (out_dtype == torch.bfloat16)
     e = rel(fg, fo)
     assert e <= (TOL_BF16_OUT if bf else TOL32), (wl.name, "fused", e)
@@ -220,17 +260,36 @@ def test_tiny_config_full():
     check(synth.tiny())
 
 
-def test_plain14_full_batch_sampled_oracle():
-    check(synth.plain14(), bs=[0, 31])
+def test_plain14_full_batch():
+    check(synth.plain14())
 
 
-def test_hier56_full_batch_sampled_oracle():
-    check(synth.hier56(), bs=[0, 63])
+def test_hier56_full_batch():
+    check(synth.hier56())
+
+
+def test_hier56_launch_live_states_every_chunk():
+    """The benchmark's launch (B = 64, 56 x 56, C = 64, 2 heads of d = 32,
+    bf16, AR(1) rows: the 64-token sub-block on four waves) on states that
+    keep every chunk alive: retention fixed at 0.999 and states of std 1.
+    With the benchmark's own states the memories contract by ~1e-9 per chunk
+    and the outputs leave fp32's range after a few chunks; here the smallest
+    chunk scale stays near 1, so every one of the 56 chunks of every route
+    and batch item is checked on its own scale."""
+    wl = synth.hier56_live()
+    yg, fg = gpu_forward(wl, flags=srnl.FLAG_FIXED_ALPHA)
+    yo, fo, y32 = oracle_forward(wl, flags=srnl.FLAG_FIXED_ALPHA, fp32=True)
+    assert np.isfinite(yg).all()
+    for s in range(4):
+        assert rel(yg[s], yo[s]) <= TOL32, (s, rel(yg[s], yo[s]))
+        n = check_chunks(yg[s], yo[s], [y[s] for y in y32], 56, f"live slot {s}")
+        assert n == 56 * wl.B          # every chunk of every item is live
+    assert rel(fg, fo) <= TOL_BF16_OUT
 
 
 @pytest.mark.parametrize("stage", [0, 1, 2, 3])
 def test_hier_sweep_stage(stage):
-    check(synth.hier_sweep()[stage], bs=[0])
+    check(synth.hier_sweep()[stage])
 
 
 def test_dense200x304_full():
@@ -399,6 +458,16 @@ def _seq(B, N, C, heads, d, seed, dtype="f32", separate_q=False):
     return x, st, q
 
 
+def _scan_1d_fp32(x, st, heads, d, q=None, chunk=0):
+    """FP32_REALISATIONS fp32 evaluations of the 1-D scan (the oracle's fp32
+    build on the inputs and on perturbed copies)."""
+    out = [oracle.scan_1d(x, st, heads, d, q, chunk=chunk, precision="f32")]
+    for k in range(1, FP32_REALISATIONS):
+        out.append(oracle.scan_1d(oracle.perturbed(x, 3 * k), oracle.perturbed(st, 3 * k + 2), heads, d,
+                                  oracle.perturbed(q, 3 * k + 1), chunk=chunk, precision="f32"))
+    return out
+
+
 def _scan_1d_gpu(x, st, heads, d, q=None, dtype="f32", chunk=0):
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     print(f"[gpu] scan_1d B={x.shape[0]} N={x.shape[1]} C={x.shape[2]} {heads}x{d} "
@@ -421,9 +490,10 @@ def test_scan_1d_matches_oracle(d, dtype, chunk):
     x, st, _ = _seq(B, N, C, heads, d, seed=40 + d, dtype=dtype)
     yg = _scan_1d_gpu(x, st, heads, d, dtype=dtype, chunk=chunk)
     yo = oracle.scan_1d(x, st, heads, d, chunk=chunk)
+    y32 = _scan_1d_fp32(x, st, heads, d, chunk=chunk)
     assert np.isfinite(yg).all()
     assert rel(yg, yo) <= TOL32, rel(yg, yo)
-    assert chunk_rel(yg, yo, chunk if chunk > 0 else 64) <= TOL_CHUNK
+    check_chunks(yg, yo, y32, chunk if chunk > 0 else 64, "1-D")
 
 
 def test_scan_1d_bench_workload_sampled():
@@ -441,9 +511,10 @@ def test_scan_1d_bench_workload_sampled():
     yg = _scan_1d_gpu(x, st, heads, d, dtype="bf16")
     sel = [0, x.shape[0] - 1]
     yo = oracle.scan_1d(x[sel], st, heads, d)
+    y32 = _scan_1d_fp32(x[sel], st, heads, d)
     assert np.isfinite(yg).all()
     assert rel(yg[sel], yo) <= TOL32
-    assert chunk_rel(yg[sel], yo, 64) <= TOL_CHUNK
+    check_chunks(yg[sel], yo, y32, 64, "1-D bench workload")
 
 
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 1000])
@@ -452,8 +523,9 @@ def test_scan_1d_lengths(N):
     x, st, _ = _seq(B, N, C, heads, d, seed=N)
     yg = _scan_1d_gpu(x, st, heads, d)
     yo = oracle.scan_1d(x, st, heads, d)
+    y32 = _scan_1d_fp32(x, st, heads, d)
     assert rel(yg, yo) <= TOL32
-    assert chunk_rel(yg, yo, 64) <= TOL_CHUNK
+    check_chunks(yg, yo, y32, 64, "1-D lengths")
 
 
 def test_scan_1d_separate_queries():
