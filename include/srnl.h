@@ -84,16 +84,14 @@ typedef enum { SRNL_F32 = 0, SRNL_BF16 = 1 } srnl_dtype;
  * stream to finish. Other entry points ignore the flag. */
 #define SRNL_FLAG_CHECK_FINITE 0x40u
 /* Keep the forward's record for the backward pass (training). srnl_scan_fwd
- * (and srnl_scan_1d, the scan of a 1 x N grid, whose backward is
- * srnl_scan_bwd on that grid with SRNL_ROUTE_ROW) also writes, into
- * params->workspace, the per-chain record that the
- * windowed backward reads (each chunk's boundary rows and closing Q, and each
- * 16-token window's opening Q, u rows and transition scalars); srnl_scan_bwd
- * called with the same arguments, flags and workspace then reads that record
- * instead of recomputing it. Applies where the windowed backward does: d = 32
- * with the readout after the write; elsewhere, and in the other entry points,
- * the flag changes nothing. The record takes srnl_scan_workspace_bytes (for
- * srnl_scan_1d, of the 1 x N grid). */
+ * (srnl_scan_1d) also writes, into params->workspace, the per-chain record
+ * that the windowed backward reads (each chunk's boundary rows and closing
+ * Q, and each 16-token window's opening Q, u rows and transition scalars);
+ * srnl_scan_bwd (srnl_scan_1d_bwd) called with the same arguments, flags and
+ * workspace then reads that record instead of recomputing it. Applies where
+ * the windowed backward does: d = 32 with the readout after the write;
+ * elsewhere, and in the other entry points, the flag changes nothing. The
+ * record takes srnl_scan_workspace_bytes (srnl_scan_1d_workspace_bytes). */
 #define SRNL_FLAG_RECORD 0x80u
 
 /* Floats of initial state per (route, head): 3d^2 + 2d. */
@@ -117,11 +115,12 @@ typedef struct {
     int chunk_col;        /* 0: chunk = H on column routes; > 0: that length */
     unsigned flags;       /* SRNL_FLAG_* */
     void *stream;         /* hipStream_t */
-    /* Device workspace for srnl_scan_fwd / srnl_scan_1d, at least
-     * srnl_scan_workspace_bytes(...) bytes (that is 0, and this may be NULL,
-     * unless SRNL_FLAG_CHECK_FINITE or SRNL_FLAG_RECORD is set), 16-byte
-     * aligned; caller-owned. With SRNL_FLAG_RECORD it starts with the forward
-     * record, which srnl_scan_bwd reads from here; otherwise scratch. */
+    /* Device workspace for srnl_scan_fwd (srnl_scan_1d), at least
+     * srnl_scan_workspace_bytes(...) (srnl_scan_1d_workspace_bytes(...))
+     * bytes (that is 0, and this may be NULL, unless SRNL_FLAG_CHECK_FINITE or
+     * SRNL_FLAG_RECORD is set), 16-byte aligned; caller-owned. With
+     * SRNL_FLAG_RECORD it starts with the forward record, which srnl_scan_bwd
+     * (srnl_scan_1d_bwd) reads from here; otherwise scratch. */
     void *workspace;
     size_t workspace_bytes;
 } srnl_params;
@@ -167,8 +166,7 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads,
  * params->workspace for these sizes and params: the forward record under
  * SRNL_FLAG_RECORD (where it applies), then 256 bytes for two counters
  * (non-finite input and output values) under SRNL_FLAG_CHECK_FINITE; 0
- * without either flag, for an empty grid or for invalid arguments. For srnl_scan_1d on [B, N, C] pass
- * H = 1, W = N and route_mask = SRNL_ROUTE_ROW.
+ * without either flag, for an empty grid or for invalid arguments.
  */
 size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
                                  unsigned route_mask, const srnl_params *params);
@@ -192,6 +190,16 @@ size_t srnl_scan_workspace_bytes(int B, int H, int W, int C, int heads, int d,
  */
 srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
                          const srnl_params *params, float *out);
+
+/*
+ * srnl_scan_1d_workspace_bytes -- params->workspace srnl_scan_1d needs (the
+ * record under SRNL_FLAG_RECORD, the counters under SRNL_FLAG_CHECK_FINITE),
+ * with the 1-D chunk default applied: srnl_scan_workspace_bytes of the 1 x N
+ * grid, route SRNL_ROUTE_ROW, chunk_row 64 when params->chunk_row is 0.
+ * 0 for NULL params, an empty sequence or invalid arguments.
+ */
+size_t srnl_scan_1d_workspace_bytes(int B, int N, int C, int heads, int d,
+                                    const srnl_params *params);
 
 /*
  * srnl_fuse -- restore and fuse [OVERVIEW Four-Directional Scanning and
@@ -248,6 +256,26 @@ srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, 
                           unsigned route_mask, const srnl_params *params,
                           const float *dy, void *workspace, size_t workspace_bytes,
                           float *dx, float *dq, float *dstates);
+
+/*
+ * srnl_scan_1d_bwd_workspace_bytes / srnl_scan_1d_bwd -- backward of
+ * srnl_scan_1d [README SRNL and VisionHOPE operator: training with
+ * autograd], with its 64-token chunk default (params->chunk_row 0): the
+ * same as srnl_scan_bwd on the 1 x N grid with route_mask SRNL_ROUTE_ROW,
+ * except for the layout of the state gradient.
+ *   x, dx, dy  [B][N][C] (x in in_dtype; dx and dy fp32);
+ *   dq         [B][N][C] fp32 when params->q is not NULL, else unused;
+ *   dstates    [heads][3d^2+2d] fp32, the layout of the 1-D states
+ *              (overwritten).
+ * Under SRNL_FLAG_RECORD the record comes from params->workspace as written
+ * by srnl_scan_1d with the same arguments and params.
+ * Errors: as srnl_scan_bwd; SRNL_ERR_PTR for NULL params.
+ */
+size_t srnl_scan_1d_bwd_workspace_bytes(int B, int N, int C, int heads, int d,
+                                        const srnl_params *params);
+srnl_status srnl_scan_1d_bwd(const void *x, int B, int N, int C, int heads, int d,
+                             const srnl_params *params, const float *dy, void *workspace,
+                             size_t workspace_bytes, float *dx, float *dq, float *dstates);
 
 /*
  * srnl_fuse_bwd_workspace_bytes / srnl_fuse_bwd -- backward of srnl_fuse:

@@ -1952,7 +1952,7 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
 template <int D, typename InT>
 srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
                             int heads, unsigned mask, const float *dy, float *ws,
-                            const BwdLayout &l, float *dx, float *dq, float *dstates)
+                            const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out)
 {
     const int R = popcount4(mask);
     const int nchains = static_cast<int>(l.chains);
@@ -2006,22 +2006,22 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
     if (p->q)
         hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dqr, dq, R, n);
     const int sz = 3 * D * D + 2 * D;
-    hipLaunchKernelGGL(states_grad_kernel, dim3(grid_for(4LL * heads * sz, 256)), dim3(256), 0, st,
-                       dstp, dstates, B, heads, R, mask, sz);
+    hipLaunchKernelGGL(states_grad_kernel, dim3(grid_for(static_cast<long long>(nr_out) * heads * sz, 256)),
+                       dim3(256), 0, st, dstp, dstates, B, heads, R, mask, sz, nr_out);
     return launch_check("scan_bwd reductions");
 }
 
 template <typename InT>
 srnl_status dispatch_scan_bwd(int d, const void *x, const srnl_params *p, int B, int H, int W,
                               int C, int heads, unsigned mask, const float *dy, float *ws,
-                              const BwdLayout &l, float *dx, float *dq, float *dstates)
+                              const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out)
 {
     switch (d) {
-    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
-    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
-    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
-    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
-    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates);
+    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
+    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
+    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
+    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
+    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
     }
     return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
 }
@@ -2083,6 +2083,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // workspace of srnl_scan_fwd with SRNL_FLAG_CHECK_FINITE: two counters
 constexpr size_t kScanCheckBytes = 256;
+
+// params of srnl_scan_1d's scan: the 1 x N grid's row route, 64-token
+// chunks unless chunk_row overrides them
+srnl_params params_1d(const srnl_params *p)
+{
+    srnl_params q = *p;
+    if (q.chunk_row == 0)
+        q.chunk_row = 64;   // the 1-D default chunk
+    q.chunk_col = 0;
+    return q;
+}
 
 }  // namespace
 
@@ -2241,11 +2252,8 @@ srnl_status srnl_scan_1d(const void *x, int B, int N, int C, int heads, int d,
     g_last_error.clear();
     if (!p)
         return fail(SRNL_ERR_PTR, "params is NULL");
-    srnl_params q = *p;
-    if (q.chunk_row == 0)
-        q.chunk_row = 64;   // the 1-D default chunk
-    q.chunk_col = 0;
-    return srnl_scan_fwd(x, B, 1, N, C, heads, d, 1u, &q, out);
+    const srnl_params q = params_1d(p);
+    return srnl_scan_fwd(x, B, 1, N, C, heads, d, SRNL_ROUTE_ROW, &q, out);
 }
 
 srnl_status srnl_fuse(const float *y, int B, int H, int W, int C, unsigned route_mask,
@@ -2286,12 +2294,16 @@ size_t srnl_scan_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int 
     return t < 0 ? 0 : static_cast<size_t>(t) * sizeof(float);
 }
 
-srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+}   // extern "C"
+
+namespace {
+// srnl_scan_bwd, with the state gradients written for route slots
+// 0 .. nr_out - 1 (4 for the 2-D operator, 1 for the 1-D one)
+srnl_status scan_bwd_impl(const void *x, int B, int H, int W, int C, int heads, int d,
                           unsigned route_mask, const srnl_params *p, const float *dy,
                           void *workspace, size_t workspace_bytes, float *dx, float *dq,
-                          float *dstates)
+                          float *dstates, int nr_out)
 {
-    g_last_error.clear();
     long long n = 0;
     srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
     if (s != SRNL_OK)
@@ -2324,8 +2336,53 @@ srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, 
     }
     float *ws = static_cast<float *>(workspace);
     if (p->in_dtype == SRNL_F32)
-        return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq, dstates);
-    return dispatch_scan_bwd<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq, dstates);
+        return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
+                                        dstates, nr_out);
+    return dispatch_scan_bwd<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
+                                       dstates, nr_out);
+}
+
+}   // namespace
+
+extern "C" {
+
+srnl_status srnl_scan_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                          unsigned route_mask, const srnl_params *p, const float *dy,
+                          void *workspace, size_t workspace_bytes, float *dx, float *dq,
+                          float *dstates)
+{
+    g_last_error.clear();
+    return scan_bwd_impl(x, B, H, W, C, heads, d, route_mask, p, dy, workspace, workspace_bytes,
+                         dx, dq, dstates, 4);
+}
+
+size_t srnl_scan_1d_workspace_bytes(int B, int N, int C, int heads, int d, const srnl_params *p)
+{
+    if (!p)
+        return 0;
+    const srnl_params q = params_1d(p);
+    return srnl_scan_workspace_bytes(B, 1, N, C, heads, d, SRNL_ROUTE_ROW, &q);
+}
+
+size_t srnl_scan_1d_bwd_workspace_bytes(int B, int N, int C, int heads, int d,
+                                        const srnl_params *p)
+{
+    if (!p)
+        return 0;
+    const srnl_params q = params_1d(p);
+    return srnl_scan_bwd_workspace_bytes(B, 1, N, C, heads, d, SRNL_ROUTE_ROW, &q);
+}
+
+srnl_status srnl_scan_1d_bwd(const void *x, int B, int N, int C, int heads, int d,
+                             const srnl_params *p, const float *dy, void *workspace,
+                             size_t workspace_bytes, float *dx, float *dq, float *dstates)
+{
+    g_last_error.clear();
+    if (!p)
+        return fail(SRNL_ERR_PTR, "params is NULL");
+    const srnl_params q = params_1d(p);
+    return scan_bwd_impl(x, B, 1, N, C, heads, d, SRNL_ROUTE_ROW, &q, dy, workspace,
+                         workspace_bytes, dx, dq, dstates, 1);
 }
 
 size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_mask)

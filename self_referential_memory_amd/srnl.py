@@ -26,8 +26,10 @@ FLAG_FREEZE_KV = 0x20
 FLAG_CHECK_FINITE = 0x40
 FLAG_RECORD = 0x80
 
-EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
-           "srnl_scan_bwd_workspace_bytes", "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
+EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d",
+           "srnl_scan_1d_workspace_bytes", "srnl_fuse", "srnl_scan_bwd",
+           "srnl_scan_bwd_workspace_bytes", "srnl_scan_1d_bwd", "srnl_scan_1d_bwd_workspace_bytes",
+           "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
            "srnl_route_gather", "srnl_init_states", "srnl_block_fwd",
            "srnl_block_workspace_bytes",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
@@ -83,6 +85,12 @@ def lib() -> ctypes.CDLL:
         L.srnl_scan_bwd_workspace_bytes.restype = sz
         L.srnl_scan_bwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp, vp, sz,
                                     vp, vp, vp]
+        L.srnl_scan_1d_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(Params)]
+        L.srnl_scan_1d_workspace_bytes.restype = sz
+        L.srnl_scan_1d_bwd_workspace_bytes.argtypes = [i, i, i, i, i, ctypes.POINTER(Params)]
+        L.srnl_scan_1d_bwd_workspace_bytes.restype = sz
+        L.srnl_scan_1d_bwd.argtypes = [vp, i, i, i, i, i, ctypes.POINTER(Params), vp, vp, sz,
+                                       vp, vp, vp]
         L.srnl_fuse_bwd_workspace_bytes.argtypes = [i, i, i, i, u]
         L.srnl_fuse_bwd_workspace_bytes.restype = sz
         L.srnl_fuse_bwd.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp, sz, vp]
@@ -92,7 +100,8 @@ def lib() -> ctypes.CDLL:
         L.srnl_block_workspace_bytes.restype = sz
         L.srnl_block_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params),
                                      ctypes.POINTER(BlockWeights), vp, sz, vp]
-        for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd", "srnl_fuse_bwd",
+        for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
+                  "srnl_scan_1d_bwd", "srnl_fuse_bwd",
                   "srnl_route_gather", "srnl_init_states", "srnl_block_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
@@ -183,21 +192,19 @@ def make_params(states: torch.Tensor, x: torch.Tensor, q: Optional[torch.Tensor]
                   chunk_col, flags, _stream(stream))
 
 
-def _finite_check_workspace(p: Params, x: torch.Tensor, B, H, W, C, heads, d, route_mask):
-    """With SRNL_FLAG_CHECK_FINITE and no caller workspace, allocate one and
-    point p at it; the call waits for its stream when checking, so the buffer
-    outlives its use. Returns the tensor (None when nothing was allocated).
-    A record (SRNL_FLAG_RECORD) must outlive the call: that takes
-    scan_fwd_record or a caller workspace."""
-    if p.workspace:
-        return None
-    nbytes = lib().srnl_scan_workspace_bytes(B, H, W, C, heads, d, route_mask, ctypes.byref(p))
-    if not nbytes:
+def _finite_check_workspace(p: Params, x: torch.Tensor, nbytes: int):
+    """With SRNL_FLAG_CHECK_FINITE and no caller workspace, allocate one of
+    nbytes (the entry point's workspace query) and point p at it; the call
+    waits for its stream when checking, so the buffer outlives its use.
+    Returns the tensor (None when nothing was allocated). A record
+    (SRNL_FLAG_RECORD) must outlive the call: that takes scan_fwd_record
+    (scan_1d_record) or a caller workspace."""
+    if p.workspace or not nbytes:
         return None
     if p.flags & FLAG_RECORD and nbytes > (256 if p.flags & FLAG_CHECK_FINITE else 0):
         raise ValueError("FLAG_RECORD needs a workspace that outlives the call: use "
-                         "scan_fwd_record, which returns the record, or pass params "
-                         "with a workspace")
+                         "scan_fwd_record (scan_1d_record), which returns the record, or "
+                         "pass params with a workspace")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
     return ws
@@ -215,7 +222,9 @@ def scan_fwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         out = torch.empty((R, B, H * W, C), dtype=torch.float32, device=x.device)
     _expect(out, (R, B, H * W, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, **kw)
-    ws = _finite_check_workspace(p, x, B, H, W, C, heads, d, route_mask)
+    nbytes = 0 if p.workspace else lib().srnl_scan_workspace_bytes(
+        B, H, W, C, heads, d, route_mask, ctypes.byref(p))
+    ws = _finite_check_workspace(p, x, nbytes)
     try:
         _check(lib().srnl_scan_fwd(_ptr(x), B, H, W, C, heads, d, route_mask,
                                    ctypes.byref(p), _ptr(out)), "srnl_scan_fwd")
@@ -262,7 +271,9 @@ def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         out = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
     _expect(out, (B, N, C), torch.float32, "out")
     p = params if params is not None else make_params(states, x, q, chunk_row=chunk, **kw)
-    ws = _finite_check_workspace(p, x, B, 1, N, C, heads, d, 1)
+    nbytes = 0 if p.workspace else lib().srnl_scan_1d_workspace_bytes(
+        B, N, C, heads, d, ctypes.byref(p))
+    ws = _finite_check_workspace(p, x, nbytes)
     try:
         _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
                "srnl_scan_1d")
@@ -270,6 +281,56 @@ def scan_1d(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
         if ws is not None:
             p.workspace, p.workspace_bytes = None, 0
     return out
+
+
+def scan_1d_record(x: torch.Tensor, states: torch.Tensor, heads: int, d: int,
+                   q: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, *,
+                   chunk: int = 0, flags: int = 0, **kw):
+    """srnl_scan_1d with SRNL_FLAG_RECORD: y [B,N,C] and the forward record
+    (a uint8 device tensor, or None where the windowed backward does not
+    apply) for scan_1d_bwd(..., record=...)."""
+    B, N, C = x.shape
+    _expect(states, (heads, 3 * d * d + 2 * d), torch.float32, "states")
+    if out is None:
+        out = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
+    _expect(out, (B, N, C), torch.float32, "out")
+    p = make_params(states, x, q, chunk_row=chunk, flags=flags | FLAG_RECORD, **kw)
+    only = Params.from_buffer_copy(p)
+    only.flags &= ~FLAG_CHECK_FINITE
+    rec_bytes = lib().srnl_scan_1d_workspace_bytes(B, N, C, heads, d, ctypes.byref(only))
+    nbytes = lib().srnl_scan_1d_workspace_bytes(B, N, C, heads, d, ctypes.byref(p))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    if ws is not None:
+        p.workspace, p.workspace_bytes = ws.data_ptr(), nbytes
+    _check(lib().srnl_scan_1d(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(out)),
+           "srnl_scan_1d")
+    return out, (ws[:rec_bytes] if rec_bytes else None)
+
+
+def scan_1d_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, dy: torch.Tensor,
+                q: Optional[torch.Tensor] = None, *, chunk: int = 0,
+                record: Optional[torch.Tensor] = None, **kw):
+    """srnl_scan_1d_bwd: dy [B,N,C] fp32 -> (dx [B,N,C], dq or None, dstates
+    [heads,3d^2+2d]), all fp32, for srnl_scan_1d's forward with the same
+    arguments (chunk 0 selects 64 tokens). ``record``: the forward record
+    from scan_1d_record. The workspace is allocated here (torch)."""
+    B, N, C = x.shape
+    _expect(states, (heads, 3 * d * d + 2 * d), torch.float32, "states")
+    _expect(dy, (B, N, C), torch.float32, "dy")
+    p = make_params(states, x, q, chunk_row=chunk, **kw)
+    if record is not None:
+        p.flags = (p.flags | FLAG_RECORD) & ~FLAG_CHECK_FINITE
+        p.workspace, p.workspace_bytes = record.data_ptr(), record.numel() * record.element_size()
+    nbytes = lib().srnl_scan_1d_bwd_workspace_bytes(B, N, C, heads, d, ctypes.byref(p))
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
+    dx = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
+    dq = None if q is None else torch.empty_like(dx)
+    dst = torch.empty((heads, 3 * d * d + 2 * d), dtype=torch.float32, device=x.device)
+    _check(lib().srnl_scan_1d_bwd(_ptr(x), B, N, C, heads, d, ctypes.byref(p), _ptr(dy),
+                                  _ptr(ws), int(nbytes), _ptr(dx), _ptr(dq), _ptr(dst)),
+           "srnl_scan_1d_bwd")
+    _keep_for_stream(p.stream, ws)
+    return dx, dq, dst
 
 
 def fuse(y: torch.Tensor, B: int, H: int, W: int, C: int, route_mask: int,
@@ -366,19 +427,44 @@ def forward(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: 
                 stream=kw.get("stream"))
 
 
+def _side_stream(kw):
+    """The stream kw asks for when it is not the current one, else None."""
+    s = kw.get("stream")
+    if s is None:
+        return None
+    cur = torch.cuda.current_stream()
+    return None if (s.cuda_stream or 0) == (cur.cuda_stream or 0) else s
+
+
 class Operator(torch.autograd.Function):
     """The operator (scan + fuse) as an autograd node: the forward pass is
     srnl_scan_fwd and srnl_fuse, the backward pass srnl_fuse_bwd and
     srnl_scan_bwd. Gradients flow to x, the initial states, the scales and
     the separate queries. The route outputs are kept for the fusion backward,
     and, where the windowed backward applies, the forward's record
-    (SRNL_FLAG_RECORD), so the backward does not run the forward again."""
+    (SRNL_FLAG_RECORD), so the backward does not run the forward again.
+
+    With stream= (kw) another than the current stream, both passes run on
+    that stream: it first waits for the current stream (the inputs, or the
+    incoming gradient, are made there), everything the pass allocates is
+    allocated on it, and the current stream then waits for it before the
+    result is handed back; the results are recorded as used on the current
+    stream, so the caching allocator keeps them until that stream is done."""
 
     @staticmethod
     def forward(ctx, x, states, scales, q, heads, d, route_mask, kw):
         B, H, W, C = x.shape
-        y, rec = scan_fwd_record(x, states, heads, d, route_mask, q, **kw)
-        out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype, stream=kw.get("stream"))
+        side = _side_stream(kw)
+        kwc = {k: v for k, v in kw.items() if k != "stream"}
+        cur = torch.cuda.current_stream()
+        if side is not None:
+            side.wait_stream(cur)
+        with torch.cuda.stream(side if side is not None else cur):
+            y, rec = scan_fwd_record(x, states, heads, d, route_mask, q, **kwc)
+            out = fuse(y, B, H, W, C, route_mask, scales, out_dtype=x.dtype)
+        if side is not None:
+            cur.wait_stream(side)
+            out.record_stream(cur)
         ctx.save_for_backward(x, states, scales, q, y, rec)
         ctx.cfg = (heads, d, route_mask, kw)
         return out
@@ -388,11 +474,23 @@ class Operator(torch.autograd.Function):
         x, states, scales, q, y, rec = ctx.saved_tensors
         heads, d, route_mask, kw = ctx.cfg
         B, H, W, C = x.shape
-        dout = dout.to(torch.float32).contiguous()
-        dyr, dsc = fuse_bwd(dout, y, B, H, W, C, route_mask, scales, stream=kw.get("stream"))
-        dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, record=rec, **kw)
-        return (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype),
-                None, None, None, None)
+        side = _side_stream(kw)
+        kwc = {k: v for k, v in kw.items() if k != "stream"}
+        cur = torch.cuda.current_stream()
+        if side is not None:
+            side.wait_stream(cur)
+            dout.record_stream(side)
+        with torch.cuda.stream(side if side is not None else cur):
+            d32 = dout.to(torch.float32).contiguous()
+            dyr, dsc = fuse_bwd(d32, y, B, H, W, C, route_mask, scales)
+            dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, record=rec, **kwc)
+            grads = (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype))
+        if side is not None:
+            cur.wait_stream(side)
+            for g in grads:
+                if g is not None:
+                    g.record_stream(cur)
+        return grads + (None, None, None, None)
 
 
 def operator(x: torch.Tensor, states: torch.Tensor, scales: torch.Tensor, heads: int, d: int,

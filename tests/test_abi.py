@@ -169,6 +169,36 @@ def test_scan_1d_null_params_and_empty_sequence():
     assert L.srnl_scan_1d(None, 1, 4, 8, 2, 4, None, None) == srnl.SRNL_ERR_PTR
     assert _scan_1d(N=0) == srnl.SRNL_OK      # empty sequence: no-op, no pointer needed
     assert _scan_1d(B=0) == srnl.SRNL_OK
+    assert L.srnl_scan_1d_bwd(None, 1, 4, 8, 2, 4, None, None, None, 0, None, None,
+                              None) == srnl.SRNL_ERR_PTR
+    p = srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, 0, None)
+    assert L.srnl_scan_1d_bwd(None, 0, 4, 8, 2, 4, ctypes.byref(p), None, None, 0, None, None,
+                              None) == srnl.SRNL_OK
+    assert L.srnl_scan_1d_workspace_bytes(1, 4, 8, 2, 4, None) == 0
+    assert L.srnl_scan_1d_bwd_workspace_bytes(1, 4, 8, 2, 4, None) == 0
+
+
+@pytest.mark.parametrize("chunk", [0, 100])
+def test_scan_1d_workspace_queries_apply_the_1d_chunk(chunk):
+    """The 1-D queries size the record and the backward's workspace for the
+    chunks srnl_scan_1d runs: 64 tokens when chunk_row is 0 (the 2-D query on
+    the 1 x N grid would read 0 as one chunk of N tokens)."""
+    L = srnl.lib()
+    B, N, C, heads, d = 2, 300, 64, 2, 32
+    eff = chunk if chunk > 0 else 64
+    for flags in (srnl.FLAG_RECORD, srnl.FLAG_RECORD | srnl.FLAG_CHECK_FINITE, 0):
+        p1 = srnl.Params(None, None, 0, 0.9, 1e-6, chunk, 0, flags, None)
+        p2 = srnl.Params(None, None, 0, 0.9, 1e-6, eff, 0, flags, None)
+        a = L.srnl_scan_1d_workspace_bytes(B, N, C, heads, d, ctypes.byref(p1))
+        b = L.srnl_scan_workspace_bytes(B, 1, N, C, heads, d, 1, ctypes.byref(p2))
+        assert a == b
+        a = L.srnl_scan_1d_bwd_workspace_bytes(B, N, C, heads, d, ctypes.byref(p1))
+        b = L.srnl_scan_bwd_workspace_bytes(B, 1, N, C, heads, d, 1, ctypes.byref(p2))
+        assert a == b and a > 0
+    p0 = srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, srnl.FLAG_RECORD, None)
+    whole = L.srnl_scan_workspace_bytes(B, 1, N, C, heads, d, 1, ctypes.byref(p0))
+    if chunk == 0:
+        assert L.srnl_scan_1d_workspace_bytes(B, N, C, heads, d, ctypes.byref(p0)) != whole
 
 
 def _block(B=1, H=2, W=2, C=64, heads=2, d=32, mask=15, q=None, F=128, eps=1e-5,

@@ -377,3 +377,78 @@ def test_forward_record_with_finite_check():
         srnl.scan_fwd_record(xb, st, wl.heads, wl.d, 15, flags=srnl.FLAG_CHECK_FINITE)
     assert e.value.status == srnl.SRNL_ERR_NONFINITE
     assert "1 non-finite input values" in str(e.value)
+
+
+@pytest.mark.parametrize("chunk,record,dtype,separate_q", [
+    (0, True, "bf16", False), (0, False, "f32", False), (100, True, "f32", True)])
+def test_scan_1d_backward_matches_oracle(chunk, record, dtype, separate_q):
+    """srnl_scan_1d_bwd after srnl_scan_1d (with the forward keeping its
+    record, or the backward recording it itself), 64-token default chunks or
+    a 100-token override, 300 tokens (a short final chunk), against the
+    gradient oracle on the 1 x N grid's row route; the state gradient comes
+    back in the 1-D layout [heads][3d^2+2d]."""
+    B, N, C, heads, d = 2, 300, 64, 2, 32
+    print(f"[gpu] 1-D backward chunk={chunk} record={record} {dtype} q={separate_q}", flush=True)
+    wl = _wl("g1d", B, 1, N, heads, d, dtype=dtype, seed=31, state_std=0.5,
+             separate_q=separate_q)
+    st1 = np.ascontiguousarray(wl.states[0])
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(wl.x.reshape(B, N, C)).to(DEV).to(dt)
+    q = None if wl.q is None else torch.from_numpy(wl.q.reshape(B, N, C)).to(DEV).to(dt)
+    st = torch.from_numpy(st1).to(DEV)
+    dyd = np.random.default_rng(31).standard_normal((B, N, C)).astype(np.float32)
+    dy = torch.from_numpy(dyd).to(DEV)
+    if record:
+        y, rec = srnl.scan_1d_record(x, st, heads, d, q, chunk=chunk)
+        assert rec is not None
+    else:
+        y, rec = srnl.scan_1d(x, st, heads, d, q, chunk=chunk), None
+    dx, dq, dst = srnl.scan_1d_bwd(x, st, heads, d, dy, q, chunk=chunk, record=rec)
+    torch.cuda.synchronize()
+    assert torch.equal(y, srnl.scan_1d(x, st, heads, d, q, chunk=chunk))
+    st4 = np.zeros((4,) + st1.shape, np.float32)
+    st4[0] = st1
+    gx, gq, gst, _ = G.grads(wl.x, st4, np.ones((4, C), np.float32), heads, d, 1, wl.q,
+                             dy=dyd.reshape(1, B, N, C), dfused=None,
+                             chunk_row=chunk if chunk > 0 else 64, chunk_col=0)
+    assert tuple(dst.shape) == (heads, 3 * d * d + 2 * d)
+    assert rel(dx.cpu().numpy(), gx.reshape(B, N, C)) <= TOL, "dx"
+    assert rel(dst.cpu().numpy(), gst[0]) <= TOL, "dstates"
+    assert not gst[1:].any()
+    if q is not None:
+        assert rel(dq.cpu().numpy(), gq.reshape(B, N, C)) <= TOL, "dq"
+    # the same gradients as the 2-D backward on the 1 x N grid with the chunk
+    # spelled out
+    dx2, dq2, dst2 = srnl.scan_bwd(x.view(B, 1, N, C), torch.from_numpy(st4).to(DEV), heads, d,
+                                   dy.view(1, B, N, C), 1,
+                                   None if q is None else q.view(B, 1, N, C),
+                                   chunk_row=chunk if chunk > 0 else 64)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2.view(B, N, C)) and torch.equal(dst, dst2[0])
+
+
+def test_autograd_operator_on_a_side_stream_matches():
+    """srnl.operator(..., stream=side): the forward output and every
+    gradient equal, bitwise, those of the same node on the current stream.
+    The side stream waits for the inputs made on the current stream, and the
+    current stream for the results (no synchronisation in between here)."""
+    print("[gpu] autograd node on a side stream", flush=True)
+    wl = _wl("gauto_side", 2, 9, 11, 2, 32, dtype="bf16", seed=33, separate_q=True)
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps)
+
+    def run(stream):
+        x = torch.from_numpy(wl.x).to(DEV).to(torch.bfloat16).requires_grad_()
+        q = torch.from_numpy(wl.q).to(DEV).to(torch.bfloat16).requires_grad_()
+        st = torch.from_numpy(wl.states).to(DEV).requires_grad_()
+        sc = torch.from_numpy(wl.scales).to(DEV).requires_grad_()
+        out = srnl.operator(x, st, sc, wl.heads, wl.d, 15, q, stream=stream, **kw)
+        g = (out.float() * 0.5 + 1.0).to(torch.bfloat16)     # made on the current stream
+        out.backward(g)
+        return [t.clone() for t in (out, x.grad, q.grad, st.grad, sc.grad)]
+
+    ref = run(None)
+    side = torch.cuda.Stream()
+    got = run(side)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)

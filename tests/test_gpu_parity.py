@@ -665,3 +665,31 @@ def test_check_finite_flag_1d():
         srnl.scan_1d(xb, stg, 2, 32, flags=flag)
     assert e.value.status == srnl.SRNL_ERR_NONFINITE
     assert "1 non-finite input values" in str(e.value)
+
+
+@pytest.mark.parametrize("case", ["chunk100", "dense200x304"])
+def test_forward_record_outputs_on_long_chunks(case):
+    """The forward that keeps its record (SRNL_FLAG_RECORD) runs 64-token
+    sub-blocks on every chunk longer than 32 tokens, where the plain forward
+    may take 128-token ones: its outputs against the oracle on chunks that
+    span several sub-blocks (100-token chunks; the dense map's 304- and
+    200-token rows and columns, x50 outlier tokens)."""
+    if case == "chunk100":
+        wl = synth.make("rec100", 2, 12, 50, 64, 2, 32, "bf16", 41, state_std=0.5,
+                        chunk_row=100, chunk_col=100)
+    else:
+        wl = synth.dense200x304()
+    print(f"[gpu] record outputs {case}", flush=True)
+    x = _dev(wl.x, torch.bfloat16)
+    st = _dev(wl.states, torch.float32)
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15, alpha_max=wl.alpha_max,
+                                  eps=wl.eps, chunk_row=wl.chunk_row, chunk_col=wl.chunk_col)
+    torch.cuda.synchronize()
+    assert rec is not None
+    yg = y.double().cpu().numpy()
+    yo, _, y32 = oracle_forward(wl, fp32=True)
+    assert np.isfinite(yg).all()
+    for s in range(4):
+        assert rel(yg[s], yo[s]) <= TOL32, (s, rel(yg[s], yo[s]))
+        L = min(oracle.chunk_len(s, wl.H, wl.W, wl.chunk_row, wl.chunk_col), wl.N)
+        check_chunks(yg[s], yo[s], [y[s] for y in y32], L, f"record {case} slot {s}")
