@@ -29,12 +29,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_FILE = os.path.join(PROFILES, "hier56_pmc_counters.json")
 SRC = os.path.join(ROOT, "self_referential_memory_amd", "csrc", "srnl.hip")
 
-# Published MI355X peaks used for the rooflines (dense MFMA fp32 and bf16; the
-# fp32 vector peak is the same figure as the fp32 MFMA one).
+# Published MI355X peaks used for the rooflines (dense MFMA fp32 and bf16)
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
-PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+CU_NUM = 256
+XCDS = 8                        # GRBM_GUI_ACTIVE reads as the sum over the XCDs
+PCT_REPS = 50                   # per-step samples behind the median and p10/p90
 COPY_PROBE_BYTES = 1 << 30      # one plain device-to-device copy of 1 GiB ...
 COPY_PROBE_REPS = 3             # ... done this many times after the timed steps
 
@@ -51,6 +52,8 @@ PMC_PASSES = (
               "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")),
     ("insts", ("SQ_INSTS_VALU_MFMA_F32", "SQ_INSTS_VALU_MFMA_BF16", "SQ_LDS_BANK_CONFLICT",
                "SQ_LDS_IDX_ACTIVE")),
+    ("valu", ("SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+              "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")),
 )
 KERNEL_KEYS = (("scan_kernel", "scan_mfma_kernel<32"), ("fuse_kernel", "fuse_kernel"),
                ("gather_kernel", "gather_kernel"))
@@ -166,6 +169,16 @@ def pmc_summary(root: str, command: str) -> None:
                              "wr_req": nwr, "wr_64B": w64})
         if dur[name]:
             k["hbm_GBs"] = (fb + wb) / dur[name] / 1e9
+        v = per_kernel(passes["valu"], key)
+        if v is not None:
+            # rocprof's VALUBusy: quad-cycles of VALU work summed over the
+            # SIMDs (four per CU), per CU, over the active cycles of one XCD
+            cyc = v["GRBM_GUI_ACTIVE"] / XCDS
+            k["valu"] = {"busy": v["SQ_ACTIVE_INST_VALU"] / CU_NUM / cyc,
+                         "lds_busy": v["SQ_ACTIVE_INST_LDS"] / CU_NUM / cyc,
+                         "wait_inst_frac": v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+                         "active_inst_frac": v["SQ_ACTIVE_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+                         "raw": v}
         m = per_kernel(passes["mfma"], key)
         extra = per_kernel(passes["insts"], key)
         if m is not None and extra is not None:
@@ -187,21 +200,118 @@ def pmc_summary(root: str, command: str) -> None:
     print(json.dumps(out, indent=2))
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (lscpu, else /proc/cpuinfo) and core counts."""
+    import subprocess
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": aff}
+
+
+def oracle_threads() -> int:
+    """Threads for the all-core oracle figure: the cores this process may run
+    on, at most 16 (a one-GPU machine's CPU share)."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(16, aff or 1))
+
+
 def cpu_baseline(wl, n_items: int):
+    """The oracle, unchanged, on batch items 0..n_items-1: once on one thread
+    (the reported value) and once with the batch split over oracle_threads()
+    threads (the all-core figure; ctypes releases the GIL, each thread runs
+    the single-threaded oracle on its own items). Returns the record and the
+    all-core run's route outputs."""
     import numpy as np
     import oracle
     n_items = min(n_items, wl.B)
     sample = wl.x[:n_items]
+    kw = dict(alpha_max=wl.alpha_max, eps=wl.eps)
     t0 = time.perf_counter()
-    y = oracle.scan(sample, wl.states, wl.heads, wl.d, 15, alpha_max=wl.alpha_max, eps=wl.eps)
+    y = oracle.scan(sample, wl.states, wl.heads, wl.d, 15, **kw)
     oracle.fuse(y, n_items, wl.H, wl.W, wl.C, 15, wl.scales)
     dt = time.perf_counter() - t0
+    nt = oracle_threads()
+    t1 = time.perf_counter()
+    ya = oracle.scan(sample, wl.states, wl.heads, wl.d, 15, threads=nt, **kw)
+    oracle.fuse(ya, n_items, wl.H, wl.W, wl.C, 15, wl.scales)
+    dta = time.perf_counter() - t1
+    assert np.array_equal(y, ya)
     units = n_items * wl.H * wl.W * wl.heads
     what = ("the whole batch" if n_items == wl.B else
             f"batch items 0..{n_items - 1} of {wl.B}")
-    return {"value": units / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what} (all 4 routes, {wl.heads} heads, {wl.H}x{wl.W}), scan + fuse, "
-                      f"single-threaded double-precision oracle, {dt:.1f} s"}
+    rec = {"value": units / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
+           "sample": f"{what} (all 4 routes, {wl.heads} heads, {wl.H}x{wl.W}), scan + fuse, "
+                     f"single-threaded double-precision oracle, {dt:.1f} s",
+           "all_cores": {"value": units / dta, "cores": nt, "seconds": dta,
+                         "how": "the same oracle on the same items, batch split over "
+                                f"{nt} threads"}}
+    rec.update(host_cpu())
+    return rec, ya
+
+
+def oracle_check(wl, yg, fused_g, yo) -> dict:
+    """Largest error of the GPU's route outputs (yg, [R][n][N][C] for the
+    first n batch items) against the oracle's (yo): globally per route slot
+    (max |g - o| / max |o|), per chunk on each live chunk's own scale, and of
+    the fused output in its stored dtype."""
+    import numpy as np
+    import oracle
+    n = yo.shape[1]
+    glob, chunk = 0.0, 0.0
+    for s in range(yo.shape[0]):
+        o, g = yo[s], yg[s]
+        glob = max(glob, float(np.abs(g - o).max() / np.abs(o).max()))
+        L = wl.chunk_row or wl.W if s < 2 else wl.chunk_col or wl.H
+        for c0 in range(0, wl.N, L):
+            m = np.abs(o[:, c0:c0 + L]).max(axis=(1, 2))
+            e = np.abs(g[:, c0:c0 + L] - o[:, c0:c0 + L]).max(axis=(1, 2))
+            live = m > 1e-20
+            if live.any():
+                chunk = max(chunk, float((e[live] / m[live]).max()))
+    fo = oracle.fuse(yo, n, wl.H, wl.W, wl.C, 15, wl.scales)
+    ef = float(np.abs(fused_g[:n] - fo).max() / np.abs(fo).max())
+    return {"items": n, "max_rel_err_routes": glob, "max_rel_err_chunk": chunk,
+            "max_rel_err_fused_bf16": ef, "bars": {"routes": 1e-4, "fused_bf16": 2e-2}}
+
+
+def control_activity(wl, n_items: int) -> dict:
+    """How often the two stability controls act on the timed workload, from
+    the oracle's per-token trace over batch items 0..n_items-1, per token x
+    head x route: the injection cap is active where eta g > 1 - alpha (the
+    uncapped step would leave the margin; the hard-clamp ablation would cut
+    it there), the spectral clamp where it lowers the capped step."""
+    import numpy as np
+    import oracle
+    n = min(n_items, wl.B)
+    _, tr = oracle.scan(wl.x[:n], wl.states, wl.heads, wl.d, 15, alpha_max=wl.alpha_max,
+                        eps=wl.eps, trace=True, threads=oracle_threads())
+    alpha, eta, eta1, eta2, g = (tr[..., k] for k in (10, 11, 12, 13, 14))
+    return {"items": n, "units": int(alpha.size),
+            "cap_active_frac": float((eta * g > 1.0 - alpha).mean()),
+            "clamp_active_frac": float((eta2 < eta1).mean()),
+            "soft_cap_mean_ratio": float((eta1 / eta).mean())}
+
+
+def percentiles(v) -> dict:
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
 
 def seq1d_workload():
@@ -580,7 +690,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-items", type=int, default=64,
                     help="batch items the CPU-baseline oracle runs on (64 = the whole batch)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle: no CPU baseline, no oracle check, no control activity")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="hier56: skip the live-state timing and the control-activity trace "
+                         "(profiler runs)")
     ap.add_argument("--no-train-step", action="store_true",
                     help="hier56_bwd: skip the training-step timing (kernel traces of the "
                          "backward alone)")
@@ -663,6 +777,47 @@ def main():
     dt = time.perf_counter() - t0
     scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     fuse_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    fused_g = out.double().cpu().numpy() if not args.no_cpu_baseline else None
+    y_last = y.double().cpu().numpy() if not args.no_cpu_baseline else None
+
+    # per-step HIP-event samples for the median and p10/p90: the timed steps,
+    # then more steps after the timed region until there are PCT_REPS
+    more = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+            for _ in range(max(0, PCT_REPS - args.steps))]
+    for ev in more:
+        step(ev)
+    torch.cuda.synchronize()
+    samples = list(evs) + more
+    timing = {"step_ms": percentiles([e[0].elapsed_time(e[2]) for e in samples]),
+              "scan_ms": percentiles([e[0].elapsed_time(e[1]) for e in samples]),
+              "fuse_ms": percentiles([e[1].elapsed_time(e[2]) for e in samples]),
+              "what": "HIP events on the launch stream around each step (scan + fuse), "
+                      f"the {args.steps} timed steps and {len(more)} more after them"}
+
+    # the same launch on states that keep every chunk alive (retention fixed
+    # at 0.999, states of std 1): the scan's time does not depend on values
+    live = None
+    if not args.no_extras:
+        wlv = synth.hier56_live()
+        xv = torch.from_numpy(wlv.x).to(dev).to(torch.bfloat16)
+        stv = torch.from_numpy(wlv.states).to(dev)
+        pv = srnl.make_params(stv, xv, alpha_max=wlv.alpha_max, eps=wlv.eps,
+                              flags=srnl.FLAG_FIXED_ALPHA)
+        for _ in range(3):
+            srnl.scan_fwd(xv, stv, wlv.heads, wlv.d, 15, out=y, params=pv)
+        lev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+               for _ in range(PCT_REPS)]
+        for a, b in lev:
+            a.record()
+            srnl.scan_fwd(xv, stv, wlv.heads, wlv.d, 15, out=y, params=pv)
+            b.record()
+        torch.cuda.synchronize()
+        lt = percentiles([a.elapsed_time(b) for a, b in lev])
+        live = {"workload": "hier56 launch on live states: states of std 1, retention fixed "
+                            "at 0.999 (every chunk's output stays O(1))",
+                "scan_ms": lt,
+                "ratio_to_headline_median": lt["median"] / timing["scan_ms"]["median"]}
+        del xv, stv
 
     # the standalone route gather (not part of the step: the scan gathers its
     # own tokens), timed after the steps for its bandwidth
@@ -700,11 +855,15 @@ def main():
         e = {"us": k_ms * 1000.0, "algorithmic_bytes": abytes[name], "achieved_GBs": gbs,
              "peak_GBs": PEAK_HBM_GBS, "hbm_frac": gbs / PEAK_HBM_GBS,
              "pmc_hbm_bytes": None}
+        e["valu_busy"] = None
         if prof is not None and name in prof:
             e["pmc_hbm_bytes"] = prof[name]["hbm_bytes_per_launch"]
             if "mfma" in prof[name]:
                 e["mfma_pipe_util"] = prof[name]["mfma"]["pipe_util"]
                 e["mfma_bf16_TFLOPs_generation"] = prof[name]["mfma"]["bf16_TFLOPs"]
+            if "valu" in prof[name]:
+                e["valu_busy"] = prof[name]["valu"]["busy"]
+                e["wait_inst_frac"] = prof[name]["valu"]["wait_inst_frac"]
         kernels[name] = e
     rec = {
         "metric": METRIC,
@@ -739,10 +898,18 @@ def main():
             "algorithmic_flops_per_launch": flops,
         },
         "kernels": kernels,
+        "timing": timing,
+        "value_independence": live,
         "cpu_baseline": None,
+        "oracle_check": None,
+        "controls": None,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_items)
+        rec["cpu_baseline"], yo = cpu_baseline(wl, args.cpu_items)
+        rec["oracle_check"] = oracle_check(wl, y_last[:, :yo.shape[1]], fused_g, yo)
+        del yo
+        if not args.no_extras:
+            rec["controls"] = control_activity(wl, args.cpu_items)
     print(json.dumps(rec), flush=True)
 
 
