@@ -295,6 +295,26 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y_routes, int B, int H
                           size_t workspace_bytes, void *stream);
 
 /*
+ * srnl_fuse_bwd_noalloc -- srnl_fuse_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc). It takes no workspace: the
+ * partial sums go to a device array owned by the library, one per GPU, of
+ * SRNL_FUSE_BWD_SCRATCH_BYTES, held until the process ends. The call
+ * allocates nothing; its first call on a device looks up that device's
+ * array. Results are bitwise those of srnl_fuse_bwd (same kernels, same
+ * order). Calls that overlap on one GPU (other streams, other threads)
+ * share the array and race: the caller serialises them. Errors: as
+ * srnl_fuse_bwd; SRNL_ERR_WORKSPACE when the partial sums, R x
+ * ceil(B*H*W / 256) x C x 4 bytes (srnl_fuse_bwd_workspace_bytes), exceed
+ * SRNL_FUSE_BWD_SCRATCH_BYTES, e.g. B*H*W > 2,097,152 at four routes and
+ * C = 64.
+ */
+#define SRNL_FUSE_BWD_SCRATCH_BYTES (8u << 20)
+srnl_status srnl_fuse_bwd_noalloc(const float *dout, const float *y_routes, int B, int H,
+                                  int W, int C, unsigned route_mask, const float *scales,
+                                  float *dy_routes, float *dscales, void *stream);
+
+/*
  * srnl_block_fwd -- one residual block around the operator [SUMMARY
  * paragraph on 2-D maps: a two-branch residual of a depthwise convolution
  * and SRNL, then a feed-forward network; OVERVIEW Four-Directional Scanning

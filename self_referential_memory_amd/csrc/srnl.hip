@@ -42,6 +42,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -2084,6 +2085,58 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // workspace of srnl_scan_fwd with SRNL_FLAG_CHECK_FINITE: two counters
 constexpr size_t kScanCheckBytes = 256;
 
+// Scratch of srnl_fuse_bwd_noalloc: the per-block partial sums of the scale
+// gradient live in this library-owned device array (one copy per GPU, held
+// until the process ends) instead of a caller's workspace. Every call
+// overwrites the part it uses before reading it, so nothing needs clearing;
+// calls that overlap on one GPU share the array and race. In host code the
+// array's name is a stand-in, not a device address: host code uses only the
+// address looked up once per device by fuse_bwd_scratch.
+constexpr size_t kFuseBwdScratchBytes = SRNL_FUSE_BWD_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kFuseBwdScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array, for the device that runs
+// `stream` (the current device for the null stream): looked up with that
+// device current on the first call there, then kept.
+srnl_status fuse_bwd_scratch(hipStream_t stream, float **out)
+{
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SRNL_ERR_HIP, "hipGetDevice failed");
+    }
+    dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SRNL_ERR_HIP, "hipStreamGetDevice failed");
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SRNL_ERR_ARG, "device index out of range for the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SRNL_ERR_HIP, "hipSetDevice failed");
+        }
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur)
+            (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SRNL_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                          hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float *>(g_scratch_ptr[dev]);
+    return SRNL_OK;
+}
+
 // params of srnl_scan_1d's scan: the 1 x N grid's row route, 64-token
 // chunks unless chunk_row overrides them
 srnl_params params_1d(const srnl_params *p)
@@ -2393,11 +2446,15 @@ size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_
     return static_cast<size_t>(popcount4(route_mask) * fuse_bwd_blocks(B, H, W) * C) * sizeof(float);
 }
 
-srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W, int C,
+}   // extern "C"
+
+namespace {
+// srnl_fuse_bwd with its partial sums in `workspace`, or (noalloc) in the
+// library's scratch array of this GPU
+srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W, int C,
                           unsigned route_mask, const float *scales, float *dyr, float *dscales,
-                          void *workspace, size_t workspace_bytes, void *stream)
+                          void *workspace, size_t workspace_bytes, void *stream, bool noalloc)
 {
-    g_last_error.clear();
     long long n = 0;
     srnl_status s = check_grid(B, H, W, C, route_mask, &n);
     if (s != SRNL_OK)
@@ -2408,18 +2465,31 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W
         return SRNL_OK;
     const int R = popcount4(route_mask);
     const long long nblk = fuse_bwd_blocks(B, H, W);
-    if (!workspace || workspace_bytes < static_cast<size_t>(R * nblk * C) * sizeof(float))
+    const size_t need = static_cast<size_t>(R * nblk * C) * sizeof(float);
+    if (noalloc) {
+        if (need > kFuseBwdScratchBytes)
+            return fail(SRNL_ERR_WORKSPACE,
+                        "srnl_fuse_bwd_noalloc: the partial sums need " + std::to_string(need) +
+                        " bytes, more than the library's scratch of " +
+                        std::to_string(kFuseBwdScratchBytes) + " bytes (use srnl_fuse_bwd)");
+    } else if (!workspace || workspace_bytes < need) {
         return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_fuse_bwd_workspace_bytes");
+    }
     if (nblk > 65535LL * 16)
         return fail(SRNL_ERR_ARG, "grid too large for srnl_fuse_bwd");
     if (!is_device_ptr(dout) || !is_device_ptr(y) || !is_device_ptr(scales) ||
-        !is_device_ptr(dyr) || !is_device_ptr(dscales) || !is_device_ptr(workspace))
+        !is_device_ptr(dyr) || !is_device_ptr(dscales) || (!noalloc && !is_device_ptr(workspace)))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be device memory");
     if (!aligned16(dout) || !aligned16(y) || !aligned16(scales) || !aligned16(dyr) ||
-        !aligned16(dscales) || !aligned16(workspace))
+        !aligned16(dscales) || (!noalloc && !aligned16(workspace)))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *part = static_cast<float *>(workspace);
+    if (noalloc) {
+        s = fuse_bwd_scratch(st, &part);
+        if (s != SRNL_OK)
+            return s;
+    }
     hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, dout, y,
                        scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
     s = launch_check("fuse_bwd_kernel");
@@ -2428,6 +2498,27 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W
     hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C * 64, 256)), dim3(256), 0, st, part,
                        dscales, C, route_mask, static_cast<int>(nblk));
     return launch_check("fuse_bwd_scales_kernel");
+}
+}   // namespace
+
+extern "C" {
+
+srnl_status srnl_fuse_bwd(const float *dout, const float *y, int B, int H, int W, int C,
+                          unsigned route_mask, const float *scales, float *dyr, float *dscales,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    return fuse_bwd_impl(dout, y, B, H, W, C, route_mask, scales, dyr, dscales, workspace,
+                         workspace_bytes, stream, false);
+}
+
+srnl_status srnl_fuse_bwd_noalloc(const float *dout, const float *y, int B, int H, int W, int C,
+                                  unsigned route_mask, const float *scales, float *dyr,
+                                  float *dscales, void *stream)
+{
+    g_last_error.clear();
+    return fuse_bwd_impl(dout, y, B, H, W, C, route_mask, scales, dyr, dscales, nullptr, 0,
+                         stream, true);
 }
 
 size_t srnl_block_workspace_bytes(int B, int H, int W, int C, unsigned route_mask)

@@ -29,7 +29,7 @@ FLAG_RECORD = 0x80
 EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d",
            "srnl_scan_1d_workspace_bytes", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_scan_1d_bwd", "srnl_scan_1d_bwd_workspace_bytes",
-           "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes",
+           "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes", "srnl_fuse_bwd_noalloc",
            "srnl_route_gather", "srnl_init_states", "srnl_block_fwd",
            "srnl_block_workspace_bytes",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.srnl_fuse_bwd_workspace_bytes.argtypes = [i, i, i, i, u]
         L.srnl_fuse_bwd_workspace_bytes.restype = sz
         L.srnl_fuse_bwd.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp, sz, vp]
+        L.srnl_fuse_bwd_noalloc.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp]
         L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
         L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
         L.srnl_block_workspace_bytes.argtypes = [i, i, i, i, u]
@@ -101,7 +102,7 @@ def lib() -> ctypes.CDLL:
         L.srnl_block_fwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params),
                                      ctypes.POINTER(BlockWeights), vp, sz, vp]
         for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
-                  "srnl_scan_1d_bwd", "srnl_fuse_bwd",
+                  "srnl_scan_1d_bwd", "srnl_fuse_bwd", "srnl_fuse_bwd_noalloc",
                   "srnl_route_gather", "srnl_init_states", "srnl_block_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),

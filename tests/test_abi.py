@@ -274,3 +274,13 @@ def test_binding_checks_buffer_shapes():
                       torch.zeros(4, 64))
     with pytest.raises(ValueError):
         srnl.scan_1d(torch.zeros(1, 10, 64), st, 2, 32)     # 1-D states are [heads][...]
+
+
+def test_fuse_bwd_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_work():
+    """4 routes x ceil(700 * 56 * 56 / 256) blocks x 64 channels x 4 bytes of
+    partial sums exceed the library's 8 MiB scratch: a workspace error,
+    returned before the pointers are looked at."""
+    L = srnl.lib()
+    assert L.srnl_fuse_bwd_noalloc(None, None, 700, 56, 56, 64, 15, None, None, None,
+                                   None) == srnl.SRNL_ERR_WORKSPACE
+    assert "scratch" in L.srnl_last_error().decode()
