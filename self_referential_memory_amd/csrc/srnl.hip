@@ -534,7 +534,7 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static_assert(EPL * T == NT && EPL >= 2 && EPL <= 16 && ECPL % 4 == 0, "epilogue lanes");
     static_assert(NW >= NTC, "one wave per 16 rows of Q");
     static_assert(NTC % JS == 0 && CW <= NW, "column split over whole tiles");
-    static_assert(NT >= 2 * D, "vector-memory refresh: one thread per output");
+    static_assert(NT >= 4 * D, "vector-memory refresh: at least two lanes per output");
 
     // LDS pool (floats). Arrays that are dead in a phase lend their space:
     // the k rows (dead after the epilogue, until the update writes z) hold
@@ -548,6 +548,17 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int SZ_QT = D * LDP;
     static_assert(SZ_LC <= SZ_TOK && SZ_NN <= SZ_TOK, "window tables fit");
     static constexpr bool TP_IN_ES = SZ_NN + SZ_TP <= SZ_TOK;
+    // Window-local tables: with the long sub-blocks at d = 32 each wave's
+    // epilogue covers exactly the 16 tokens of the window whose tables the
+    // same wave builds (EPL = 4, one window per wave), so no block barrier
+    // is needed between the two phases if every window's tables live in
+    // that window's own dead k and v rows (16 rows of LDP floats): L in its
+    // k rows, N (and T', when it shares the v rows) in its v rows.
+    static constexpr bool WL = SWZ && EPL == 4 && NWIN == NW;
+    static constexpr int WSTR_L = WL ? 16 * LDP : 16 * WS;   // L table stride per window
+    static constexpr int WSTR_N = WL ? 16 * LDP : 16 * NS;   // N table stride per window
+    static_assert(!WL || (16 * WS <= 16 * LDP && 16 * NS + (TP_IN_ES ? 256 : 0) <= 16 * LDP),
+                  "window tables fit the window's rows");
     static constexpr bool QT_IN_ES = SZ_QT <= SZ_TOK;
     // else, when it fits, over the x, k/z, v and k^ rows (contiguous), which
     // are dead at a chunk end once the readout has read the z rows
@@ -570,7 +581,8 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int O_KZ2 = O_XB + SZ_XB;
     static constexpr int O_QV = O_KZ2 + ((JS == 2) ? SZ_TOK : 0);
     static constexpr int O_TPX = O_QV + (HAS_Q ? SZ_TOK : 0);     // T' tables, if not in v rows
-    static constexpr int O_TP = TP_IN_ES ? O_ES + SZ_NN : O_TPX;
+    static constexpr int O_TP = TP_IN_ES ? O_ES + (WL ? 16 * NS : SZ_NN) : O_TPX;
+    static constexpr int WSTR_T = (TP_IN_ES && WL) ? 16 * LDP : 256;   // T' table stride per window
     static constexpr int O_QTX = O_TPX + (TP_IN_ES ? 0 : SZ_TP);  // Q_L^T, if on its own
     static constexpr int O_QT = QT_IN_ES ? O_ES : QT_IN_TOK ? O_XS : O_QTX;
     static constexpr int POOL = O_QTX + ((QT_IN_ES || QT_IN_TOK) ? 0 : SZ_QT);
@@ -1085,7 +1097,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 }
             }
         }
-        __syncthreads();
+        if constexpr (Cfg::WL)
+            wave_lds_sync();   // this wave's epilogue is its window's only input
+        else
+            __syncthreads();
 
         // (4) window tables, wave w for windows w, w + NW, ... (window-local
         //     token indices t, s in 0..15; lane holds s = 4 lk + i, t = lm)
@@ -1146,7 +1161,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     Rr[i] = P[i] * at;
             }
             float Nr[4], Lr[4];
-            float *lc = Lc + win * 16 * WS;
+            float *lc = Lc + win * Cfg::WSTR_L;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = 4 * lk + i;
@@ -1156,7 +1171,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 Nr[i] = BEFORE ? (lt ? P[i] * gqk[i] : 0.0f) : Rr[i] * gqk[i];
             }
             st4(lc + t * WS + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
-            st4(Nn + win * 16 * NS + t * NS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
+            st4(Nn + win * Cfg::WSTR_N + t * NS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
             if (t == 15)
                 st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
             if (lk == 0) {
@@ -1209,7 +1224,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     }
                 }
                 const float ec = -EH[tb + c];
-                float *tp = Tp + win * 256;
+                float *tp = Tp + win * Cfg::WSTR_T;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     tp[tp_index(4 * g + i, c)] = ec * xf[i];
@@ -1267,8 +1282,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 const float4 gz = ld4(GZ + tb + 4 * lk);
                 const float4 rb = ld4(RB + tb + 4 * lk);
                 const float4 ee = ld4(Et + (16 * it + lm) * ETS + et_col(16 * it + lm, tb + 4 * lk));
-                const float4 tpv = ld4(Tp + win * 256 + tp_index(lm, 4 * lk));
-                const float4 nnv = ld4(Nn + win * 16 * NS + lm * NS + 4 * lk);
+                const float4 tpv = ld4(Tp + win * Cfg::WSTR_T + tp_index(lm, 4 * lk));
+                const float4 nnv = ld4(Nn + win * Cfg::WSTR_N + lm * NS + 4 * lk);
                 const float wg = WG[win];
                 // K^^T operand of the Q update with diag(R[15]) folded in
                 // (off the window's dependency chain, unlike scaling U)
@@ -1420,18 +1435,25 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                         acc = mfma4(a[s], bq[s], acc);
                     racc[w] = acc;
                 }
+                // vector memories: two lanes per output element, each over
+                // half of the reduction index, summed by DPP (the same order
+                // in every sub-block configuration)
+                constexpr int VG = 2;
                 float vacc = 0.f;
-                const int vv = tid / D, vj = tid % D;
-                if (tid < 2 * D && !frz) {
+                const int vo = tid / VG, vpart = tid % VG;
+                const int vv = vo / D, vj = vo % D;
+                if (tid < 2 * D * VG && !frz) {
 #pragma unroll
-                    for (int k = 0; k < D / 4; ++k) {
-                        const float4 bb = ld4(Bs + ix(3 * D + vv, 4 * k));
-                        const float4 qq = ld4(Qt + ix(vj, 4 * k));
+                    for (int k = 0; k < D / (4 * VG); ++k) {
+                        const int c = 4 * (vpart * (D / (4 * VG)) + k);
+                        const float4 bb = ld4(Bs + ix(3 * D + vv, c));
+                        const float4 qq = ld4(Qt + ix(vj, c));
                         vacc = fmaf(bb.x, qq.x, vacc);
                         vacc = fmaf(bb.y, qq.y, vacc);
                         vacc = fmaf(bb.z, qq.z, vacc);
                         vacc = fmaf(bb.w, qq.w, vacc);
                     }
+                    vacc = group_sum<VG>(vacc);
                 }
                 __syncthreads();
 #pragma unroll
@@ -1445,7 +1467,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                         if (!frz || tm < NTC)
                             Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
                 }
-                if (tid < 2 * D && !frz)
+                if (tid < 2 * D * VG && vpart == 0 && !frz)
                     Bs[ix(3 * D + vv, vj)] = vacc;
             }
             reset_q();
