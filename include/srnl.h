@@ -331,11 +331,12 @@ srnl_status srnl_fuse_bwd_noalloc(const float *dout, const float *y_routes, int 
  *           nearest even); the operator runs on u and q in fp32 with every
  *           other field of params (states, alpha_max, eps, chunks, flags,
  *           stream); params->q must be NULL.
- *   C in {32, 64, 128, 192, 256}; ffn_hidden F a positive multiple of 32.
+ *   C in {32, 64, 128, 192, 256, 512} (512: the hierarchical model's last
+ *   stage); ffn_hidden F a positive multiple of 32.
  *   wq, w1, w2 are bf16 words; the products are formed exactly from them
  *   and fp32 activations, accumulated in fp32.
  *   workspace: caller-owned device memory of srnl_block_workspace_bytes
- *   (u, q, s and the route outputs, all fp32).
+ *   (u, q, s and the route outputs, and at C = 512 also h, all fp32).
  * Every pointer must be device memory, 16-byte aligned. Errors:
  * SRNL_ERR_ARG, SRNL_ERR_DTYPE, SRNL_ERR_PTR, SRNL_ERR_WORKSPACE,
  * SRNL_ERR_HIP.

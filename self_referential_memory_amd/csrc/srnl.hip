@@ -2088,8 +2088,10 @@ srnl_status check_scan_args(int B, int H, int W, int C, int heads, int d, unsign
 // Workspace of srnl_block_fwd (floats, 64-float aligned parts): u, q and the
 // fused operator output s ([B][H][W][C] each), then the route outputs
 // [R][B][H*W][C].
+// Block workspace (floats, 64-float aligned parts): u, q, the fused operator
+// output s, the route outputs y, and for the wide kernels (C > 256) h.
 struct BlockLayout {
-    long long plane = 0, o_q = 0, o_s = 0, o_y = 0, total = 0;
+    long long plane = 0, o_q = 0, o_s = 0, o_y = 0, o_h = 0, total = 0;
 };
 BlockLayout block_layout(int B, int H, int W, int C, unsigned mask)
 {
@@ -2098,7 +2100,8 @@ BlockLayout block_layout(int B, int H, int W, int C, unsigned mask)
     l.o_q = l.plane;
     l.o_s = 2 * l.plane;
     l.o_y = 3 * l.plane;
-    l.total = l.o_y + align64(static_cast<long long>(popcount4(mask)) * B * H * W * C);
+    l.o_h = l.o_y + align64(static_cast<long long>(popcount4(mask)) * B * H * W * C);
+    l.total = l.o_h + (C > 256 ? l.plane : 0);
     return l;
 }
 
@@ -2565,8 +2568,8 @@ srnl_status srnl_block_fwd(const void *x, int B, int H, int W, int C, int heads,
         return fail(SRNL_ERR_PTR, "block weights are NULL");
     if (p->q)
         return fail(SRNL_ERR_ARG, "the block forms its own queries: params->q must be NULL");
-    if (C != 32 && C != 64 && C != 128 && C != 192 && C != 256)
-        return fail(SRNL_ERR_ARG, "block channels must be 32, 64, 128, 192 or 256");
+    if (C != 32 && C != 64 && C != 128 && C != 192 && C != 256 && C != 512)
+        return fail(SRNL_ERR_ARG, "block channels must be 32, 64, 128, 192, 256 or 512");
     if (w->ffn_hidden < 32 || w->ffn_hidden % 32 != 0 || w->ffn_hidden > (1 << 16))
         return fail(SRNL_ERR_ARG, "ffn_hidden must be a positive multiple of 32, at most 65536");
     if (!(w->ln_eps > 0.0f) || !std::isfinite(w->ln_eps))
@@ -2585,11 +2588,12 @@ srnl_status srnl_block_fwd(const void *x, int B, int H, int W, int C, int heads,
         if (!aligned16(q))
             return fail(SRNL_ERR_PTR, "x, out, workspace, states and every block weight must be 16-byte aligned");
     const long long ntok = static_cast<long long>(B) * H * W;
-    float *u = static_cast<float *>(workspace), *q = u + l.o_q, *sf = u + l.o_s, *y = u + l.o_y;
+    float *u = static_cast<float *>(workspace), *q = u + l.o_q, *sf = u + l.o_s, *y = u + l.o_y,
+          *hb = u + l.o_h;
     hipStream_t st = static_cast<hipStream_t>(p->stream);
     const bool bf = p->in_dtype == SRNL_BF16;
-    s = bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, nullptr, nullptr, st, true)
-           : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, nullptr, nullptr, st, true);
+    s = bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, nullptr, hb, nullptr, st, true)
+           : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, nullptr, hb, nullptr, st, true);
     if (s != SRNL_OK)
         return s;
     srnl_params ps = *p;   // the operator reads u (fp32) with queries q
@@ -2601,8 +2605,8 @@ srnl_status srnl_block_fwd(const void *x, int B, int H, int W, int C, int heads,
     s = srnl_fuse(y, B, H, W, C, route_mask, w->scales, SRNL_F32, sf, p->stream);
     if (s != SRNL_OK)
         return s;
-    return bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, sf, out, st, false)
-              : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, sf, out, st, false);
+    return bf ? dispatch_block_kernels<uint16_t>(C, x, ntok, H, W, w, u, q, sf, hb, out, st, false)
+              : dispatch_block_kernels<float>(C, x, ntok, H, W, w, u, q, sf, hb, out, st, false);
 }
 
 srnl_status srnl_route_gather(const void *x, int B, int H, int W, int C, unsigned route_mask,

@@ -215,7 +215,7 @@ def _block(B=1, H=2, W=2, C=64, heads=2, d=32, mask=15, q=None, F=128, eps=1e-5,
     (dict(weights=False), srnl.SRNL_ERR_PTR),
     (dict(q=1), srnl.SRNL_ERR_ARG),                   # the block forms its own queries
     (dict(C=48, heads=3, d=16), srnl.SRNL_ERR_ARG),   # block channels not supported
-    (dict(C=512, heads=16, d=32), srnl.SRNL_ERR_ARG),
+    (dict(C=1024, heads=16, d=64), srnl.SRNL_ERR_ARG),
     (dict(F=40), srnl.SRNL_ERR_ARG),                  # hidden width not a multiple of 32
     (dict(F=0), srnl.SRNL_ERR_ARG),
     (dict(eps=0.0), srnl.SRNL_ERR_ARG),

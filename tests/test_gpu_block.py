@@ -100,6 +100,15 @@ def test_block_channel_widths(C, heads, d, F_):
     run_block(wl, synth.block_weights(33 + C, C, F_))
 
 
+@pytest.mark.parametrize("dtype,B,H,W_,F_", [("f32", 2, 5, 7, 256), ("bf16", 2, 7, 7, 2048)])
+def test_block_stage4_width(dtype, B, H, W_, F_):
+    """C = 512 (16 heads of d = 32), the hierarchical model's last stage: the
+    wide kernels. 5 x 7 leaves a ragged last block of tokens; 7 x 7 with
+    F = 4C is the stage-4 map."""
+    wl = synth.make(f"blk_c512_{dtype}", B, H, W_, 512, 16, 32, dtype, 36, state_std=0.5)
+    run_block(wl, synth.block_weights(36, 512, F_))
+
+
 def test_block_variants_and_route_subset():
     wl = synth.make("blk_var", 2, 7, 10, 64, 2, 32, "f32", 34, state_std=2.0, outlier_frac=0.05,
                     chunk_row=4, chunk_col=3)
