@@ -886,6 +886,30 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 
     float *const svc = SAVE ? sv.base + static_cast<long long>(chain) * sv.chain_floats : nullptr;
     const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
+    // Readout Y^T = B_c Z^T of token tile tm, channel tile tn: each lane ends
+    // with four consecutive channels of one token (a 16-byte store).
+    auto readout_tile = [&](int tm, int tn) {
+        float a[KS];
+        ldrow(KZ, tm * 16 + lm, lk * KS, a);
+        if (JS == 2) {
+            float a2[KS];
+            ldrow(KZ2, tm * 16 + lm, lk * KS, a2);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                a[s] += a2[s];
+        }
+        const int u0 = tm * 16 + lm;
+        float br[KS];
+        ldrow(Bs, tn * 16 + lm, lk * KS, br);
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = mfma4(br[s], a[s], acc);
+        if (u0 < nt) {
+            float *orow = out + (out_row0 + s0 + u0) * C + static_cast<size_t>(h) * D + 4 * lk;
+            *reinterpret_cast<float4 *>(orow + tn * 16) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
     while (true) {
         __syncthreads();   // previous sub-block is done with every token array; Bs is current
         if constexpr (SAVE) {
@@ -942,7 +966,14 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     into three bf16 parts, so three bf16 products (16x16x32) per
         //     32-wide block give the fp32 result at a third of the cost of the
         //     fp32 instruction.
-        for (int tn = wave; tn < 2 * NTC; tn += NW) {
+        //     With at least two waves per output tile (the eight-wave
+        //     sub-blocks) the token tiles of a tile are dealt out between them.
+        constexpr int GT = 2 * NTC;                        // output tiles
+        constexpr int GS = (NW >= 2 * GT) ? NW / GT : 1;   // waves per output tile
+        constexpr int NTM = NWIN / GS;                     // token tiles per wave
+        static_assert(NWIN % GS == 0, "token tiles deal out evenly");
+        const int tm_ph = (GS > 1) ? wave / GT : 0;        // this wave's token tiles tm_ph + GS k
+        for (int tn = (GS > 1) ? wave % GT : wave; tn < GT; tn += (GS > 1) ? GT : NW) {
             float *dst = (tn < NTC) ? KZ : Es;
             const int oc = (tn % NTC) * 16 + lm;
             const int brow = D + tn * 16 + lm;   // boundary row of this lane
@@ -955,24 +986,25 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     ldrow(Bs, brow, 32 * kb + 8 * lk, bv);
                     split3_bf16(bv, bh[kb], bm[kb], bl[kb]);
                 }
-                // every token tile of the sub-block (rows past nt are zero)
-                bf16x8 xa[NWIN][KB];
+                // this wave's token tiles of the sub-block (rows past nt are zero)
+                bf16x8 xa[NTM][KB];
 #pragma unroll
-                for (int tm = 0; tm < NWIN; ++tm)
+                for (int k = 0; k < NTM; ++k)
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
                         float xv[8];
-                        ldrow(Xs, tm * 16 + lm, 32 * kb + 8 * lk, xv);
-                        xa[tm][kb] = pack_bf16_exact(xv);
+                        ldrow(Xs, (tm_ph + GS * k) * 16 + lm, 32 * kb + 8 * lk, xv);
+                        xa[k][kb] = pack_bf16_exact(xv);
                     }
 #pragma unroll
-                for (int tm = 0; tm < NWIN; ++tm) {
+                for (int k = 0; k < NTM; ++k) {
+                    const int tm = tm_ph + GS * k;
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bl[kb], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bm[kb], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[tm][kb], bh[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bl[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bm[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bh[kb], acc, 0, 0, 0);
                     }
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
@@ -982,7 +1014,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 float bg[KS];
                 ldrow(Bs, brow, lk * KS, bg);
 #pragma unroll
-                for (int tm = 0; tm < NWIN; ++tm) {
+                for (int k = 0; k < NTM; ++k) {
+                    const int tm = tm_ph + GS * k;
                     float a[KS];
                     ldrow(Xs, tm * 16 + lm, lk * KS, a);
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -1357,6 +1390,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
         } else if constexpr (JS == 2) {
             // the update's per-window block barrier, for the waves outside it
+            // (their MFMA work here would share the update waves' pipes and
+            // lengthen the window chain)
             for (int win = 0; win < nwin; ++win)
                 __syncthreads();
         }
@@ -1379,30 +1414,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             constexpr bool BY_TOKENS = NW > NTC;
             const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
             const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
-            for (int tm = tm0; tm < nwin; tm += tms) {
-                float a[KS];
-                ldrow(KZ, tm * 16 + lm, lk * KS, a);
-                if (JS == 2) {
-                    float a2[KS];
-                    ldrow(KZ2, tm * 16 + lm, lk * KS, a2);
+            for (int tm = tm0; tm < nwin; tm += tms)
 #pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        a[s] += a2[s];
-                }
-                const int u0 = tm * 16 + lm;
-                float *orow = out + (out_row0 + s0 + u0) * C + static_cast<size_t>(h) * D + 4 * lk;
-#pragma unroll
-                for (int tn = tn0; tn < NTC; tn += tns) {
-                    float br[KS];
-                    ldrow(Bs, tn * 16 + lm, lk * KS, br);
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        acc = mfma4(br[s], a[s], acc);
-                    if (u0 < nt)
-                        *reinterpret_cast<float4 *>(orow + tn * 16) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                }
-            }
+                for (int tn = tn0; tn < NTC; tn += tns)
+                    readout_tile(tm, tn);
         }
 
         if (chunk_end) {
