@@ -559,15 +559,18 @@ def main_block56(args):
     print(json.dumps(rec), flush=True)
 
 
-def main_hier56_bwd(args):
-    """Backward of the hier56 step: srnl_fuse_bwd + srnl_scan_bwd for a given
-    dL/d(fused output), forward outputs and inputs resident in HBM."""
+def main_bwd(args, wl_name):
+    """Backward of a forward step: srnl_fuse_bwd + srnl_scan_bwd for a given
+    dL/d(fused output), forward outputs and inputs resident in HBM. hier56:
+    the hierarchical stage-1 map (d = 32: recording forward + windowed
+    adjoint); plain14: the plain backbone's map (B=32, 14x14, C=192, 3 heads
+    of d=64: the sequential adjoint)."""
     import numpy as np
     import torch
     from self_referential_memory_amd import srnl, synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = synth.hier56()
+    wl = synth.hier56() if wl_name == "hier56" else synth.plain14()
     x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
     st = torch.from_numpy(wl.states).to(dev)
     sc = torch.from_numpy(wl.scales).to(dev)
@@ -656,23 +659,35 @@ def main_hier56_bwd(args):
     units = wl.B * wl.H * wl.W * wl.heads
     flops = 2 * algorithmic_flops_per_unit(wl.d) * units * R
     achieved = flops / (scan_ms / 1000.0) / 1e12
+    if wl_name == "hier56":
+        what = ("hier56_bwd: backward of the hier56 step (srnl_fuse_bwd + srnl_scan_bwd), "
+                "B=64, 56x56, C=64, 2 heads x d=32, 4 routes")
+        # the d = 32 scan backward (recording forward + windowed adjoint) runs
+        # its contractions on fp32 MFMA
+        roof = {"kernel": "scan_bwd (recording forward + scan_bwd_wy_kernel)", "bound": "mfma",
+                "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP32_MFMA_TFLOPS}
+    else:
+        what = ("plain14_bwd: backward of the plain14 step (srnl_fuse_bwd + srnl_scan_bwd), "
+                "B=32, 14x14, C=192, 3 heads x d=64, 4 routes")
+        # the d = 64 scan backward is the sequential adjoint on the fp32
+        # vector units; its peak is the fp32 vector figure (157.3 TFLOP/s with
+        # two-wide fp32 instructions, which this build does not emit: half
+        # of it, 78.6, is the ceiling of the scalar fp32 FMAs it issues)
+        roof = {"kernel": "scan_bwd_kernel<64> (sequential adjoint)", "bound": "alu",
+                "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS / 2, "unit": "TFLOP/s",
+                "frac": achieved / (PEAK_FP32_MFMA_TFLOPS / 2)}
+    roof.update({"traffic": None, "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops})
     rec = {
         "metric": "SRNL bwd tokens·heads/s (4 routes) at stage shapes",
         "value": units / (ms / 1000.0), "unit": "tokens·heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "hier56_bwd: backward of the hier56 step (srnl_fuse_bwd + "
-                               "srnl_scan_bwd), B=64, 56x56, C=64, 2 heads x d=32, 4 routes",
+        "config": {"workload": what,
                    "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C, "heads": wl.heads, "d": wl.d,
                    "routes": R, "input_dtype": "bf16", "parallelism": "single GPU"},
-        # the d = 32 scan backward (recording forward + windowed adjoint) runs
-        # its contractions on fp32 MFMA
-        "roofline": {"kernel": "scan_bwd (recording forward + scan_bwd_wy_kernel)",
-                     "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                     "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops},
+        "roofline": roof,
         "cpu_baseline": None,
         "train_step": {"what": "srnl_scan_fwd + srnl_fuse (bf16 out) + srnl_fuse_bwd + "
                                "srnl_scan_bwd per step",
@@ -706,10 +721,12 @@ def main():
     ap.add_argument("--pmc-passes", action="store_true",
                     help="print the counter passes, one line each: NAME COUNTER...")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
-    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "stages", "block56"),
+    ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "plain14_bwd", "stages",
+                                           "block56"),
                     default="hier56",
                     help="hier56: the 2-D four-route operator (default); seq1d: the "
-                         "standalone 1-D SRNL; hier56_bwd: its backward pass; stages: the "
+                         "standalone 1-D SRNL; hier56_bwd, plain14_bwd: the backward pass on the "
+                         "hierarchical stage-1 and the plain-backbone maps; stages: the "
                          "forward on every stage shape; block56: one residual block around "
                          "the operator at the 56x56 shape")
     args = ap.parse_args()
@@ -731,8 +748,8 @@ def main():
     if args.workload == "block56":
         main_block56(args)
         return
-    if args.workload == "hier56_bwd":
-        main_hier56_bwd(args)
+    if args.workload in ("hier56_bwd", "plain14_bwd"):
+        main_bwd(args, args.workload[:-4])
         return
     if args.workload == "stages":
         main_stages(args)
