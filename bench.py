@@ -698,6 +698,54 @@ def main_bwd(args, wl_name):
     print(json.dumps(rec), flush=True)
 
 
+PHASES = ("load", "generation", "epilogue", "window_tables", "update", "readout", "refresh")
+
+
+def main_phase_clocks(args):
+    """Cycles per phase of the scan kernel, from the phase-clock build of the
+    library (python -m self_referential_memory_amd.build --phase-clocks):
+    wave 0 of each chain's block stamps the shader clock after every phase's
+    closing barrier. One line per workload: mean cycles per sub-block of each
+    phase over all chains, and per chain in all."""
+    import ctypes
+    import numpy as np
+    import torch
+    from self_referential_memory_amd import build as B_
+    from self_referential_memory_amd import srnl, synth
+    if not os.path.exists(B_.PHASE_LIB):
+        raise RuntimeError(f"{B_.PHASE_LIB} is missing: build it with "
+                           "python -m self_referential_memory_amd.build --phase-clocks")
+    srnl.LIB_PATH = B_.PHASE_LIB
+    L = srnl.lib()
+    L.srnl_phase_clocks.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.srnl_phase_clocks.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sweep = synth.hier_sweep()
+    wls = [synth.hier56(), synth.hier56(B=32), synth.dense200x304(), sweep[1], sweep[2],
+           sweep[3], synth.plain14()]
+    for wl in wls:
+        x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+        st = torch.from_numpy(wl.states).to(dev)
+        y = torch.empty((4, wl.B, wl.N, wl.C), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            srnl.scan_fwd(x, st, wl.heads, wl.d, 15, out=y)
+        torch.cuda.synchronize()
+        nch = 4 * wl.B * wl.heads
+        nb = (nch + 7) // 8 * 8
+        buf = np.zeros(nb * 9, dtype=np.uint64)
+        assert L.srnl_phase_clocks(buf.ctypes.data, buf.size) == 0
+        a = buf.reshape(nb, 9)[:nch].astype(np.float64)
+        nsub = float(a[:, 7].mean())
+        rec = {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C,
+               "heads": wl.heads, "d": wl.d, "chains": nch, "sub_blocks_per_chain": nsub,
+               "cycles_per_chain": float(a[:, 8].mean()),
+               "cycles_per_sub_block": {k: float(v) for k, v in
+                                        zip(PHASES, a[:, :7].mean(axis=0) / nsub)}}
+        print(json.dumps(rec), flush=True)
+        del x, y
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -721,6 +769,9 @@ def main():
     ap.add_argument("--pmc-passes", action="store_true",
                     help="print the counter passes, one line each: NAME COUNTER...")
     ap.add_argument("--pmc-command", default="", help="command recorded in the summary")
+    ap.add_argument("--phase-clocks", action="store_true",
+                    help="cycles per phase of the scan kernel on every stage shape, from the "
+                         "phase-clock build of the library")
     ap.add_argument("--workload", choices=("hier56", "seq1d", "hier56_bwd", "plain14_bwd", "stages",
                                            "block56"),
                     default="hier56",
@@ -736,6 +787,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.pmc_command)
+        return
+    if args.phase_clocks:
+        main_phase_clocks(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "srnl.hip")
 LIB = os.path.join(PKG, "libsrnl.so")
+# the same source with the scan kernel's phase clocks compiled in (a
+# measurement build, loaded only by bench.py --phase-clocks)
+PHASE_LIB = os.path.join(PKG, "libsrnl_phase.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,15 +26,17 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-o", tmp, SRC]
+def build(verbose: bool = False, phase_clocks: bool = False) -> str:
+    lib = PHASE_LIB if phase_clocks else LIB
+    tmp = lib + ".tmp"
+    extra = ["-DSRNL_PHASE_CLOCKS=1"] if phase_clocks else []
+    cmd = [HIPCC] + FLAGS + extra + ["-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_clocks="--phase-clocks" in sys.argv))

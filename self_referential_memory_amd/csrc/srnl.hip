@@ -740,6 +740,30 @@ template <int D> struct SaveLayout {
 // branch bits of a recorded token: soft-cap series, hard cap taken, clamp taken
 constexpr int SCB_SERIES = 1, SCB_HARD = 2, SCB_CLAMP = 4;
 
+// Phase clocks (a separate build with -DSRNL_PHASE_CLOCKS=1, never the
+// library itself): wave 0 of every scan block reads the shader clock right
+// after each phase's closing barrier and accumulates the cycles per phase,
+// load, generation, epilogue, window tables, update, readout, refresh, in
+// srnl_phase_buf[block][0..6], then the sub-block count [7] and the whole
+// block's cycles [8]; srnl_phase_clocks copies them out.
+#ifndef SRNL_PHASE_CLOCKS
+#define SRNL_PHASE_CLOCKS 0
+#endif
+#if SRNL_PHASE_CLOCKS
+constexpr int kPhaseBlocks = 16384;
+__device__ unsigned long long srnl_phase_buf[kPhaseBlocks * 9];
+#define SRNL_PHASE(k)                                                                \
+    do {                                                                             \
+        if (wave == 0) {                                                             \
+            const unsigned long long t_ = clock64();                                 \
+            ph_acc[k] += t_ - ph_t;                                                  \
+            ph_t = t_;                                                               \
+        }                                                                            \
+    } while (0)
+#else
+#define SRNL_PHASE(k) ((void)0)
+#endif
+
 template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false,
           bool OUT = !SAVE>
 __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
@@ -885,6 +909,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     issue_loads(s0, nt);
 
     float *const svc = SAVE ? sv.base + static_cast<long long>(chain) * sv.chain_floats : nullptr;
+#if SRNL_PHASE_CLOCKS
+    unsigned long long ph_acc[7] = {0, 0, 0, 0, 0, 0, 0}, ph_n = 0, ph_t = clock64();
+    const unsigned long long ph_t0 = ph_t;
+#endif
     const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
     // Readout Y^T = B_c Z^T of token tile tm, channel tile tn: each lane ends
     // with four consecutive channels of one token (a 16-byte store).
@@ -957,6 +985,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         if (nt1 > 0)
             issue_loads(s1, nt1);
         __syncthreads();
+        SRNL_PHASE(0);
 
         const int nwin = (nt + 15) >> 4;   // 16-token windows (= token tiles)
 
@@ -1029,6 +1058,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
         }
         __syncthreads();
+        SRNL_PHASE(1);
 
         // (3) transition scalars, EPL lanes per token [SUMMARY stabilisation]:
         //     k^ = k / sqrt(|k|^2 + eps), e = k^ - v, eta = sigmoid(b_eta . x),
@@ -1134,6 +1164,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             wave_lds_sync();   // this wave's epilogue is its window's only input
         else
             __syncthreads();
+        SRNL_PHASE(2);
 
         // (4) window tables, wave w for windows w, w + NW, ... (window-local
         //     token indices t, s in 0..15; lane holds s = 4 lk + i, t = lm)
@@ -1264,6 +1295,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
         }
         __syncthreads();
+        SRNL_PHASE(3);
 
         // (5) token-order update, window by window, on MFMA. Wave w owns rows
         //     16 it .. 16 it + 15 of Q (it = w % NTC) and, when two waves share
@@ -1396,6 +1428,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 __syncthreads();
         }
         __syncthreads();
+        SRNL_PHASE(4);
         if constexpr (!QT_EARLY && !Cfg::QT_IN_TOK) {
             if (chunk_end && cend < N) {
                 if (wave < CW)
@@ -1420,6 +1453,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     readout_tile(tm, tn);
         }
 
+        SRNL_PHASE(5);
         if (chunk_end) {
             if (cend < N) {
                 // (7) refresh the boundary: B <- B Q_L (tiles split over the
@@ -1487,6 +1521,10 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
             reset_q();
         }
+        SRNL_PHASE(6);
+#if SRNL_PHASE_CLOCKS
+        ph_n += 1;
+#endif
         if (s1 >= N)
             break;
         s0 = s1;
@@ -1494,6 +1532,14 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         cend = cend1;
         nt = nt1;
     }
+#if SRNL_PHASE_CLOCKS
+    if (wave == 0 && lane == 0 && blockIdx.x < kPhaseBlocks) {
+        for (int k = 0; k < 7; ++k)
+            srnl_phase_buf[blockIdx.x * 9 + k] = ph_acc[k];
+        srnl_phase_buf[blockIdx.x * 9 + 7] = ph_n;
+        srnl_phase_buf[blockIdx.x * 9 + 8] = clock64() - ph_t0;
+    }
+#endif
 }
 
 // ------------------------------------------------------------ finite check
@@ -2680,3 +2726,13 @@ srnl_status srnl_init_states(float *states, int heads, int d, unsigned long long
 }
 
 }  // extern "C"
+
+#if SRNL_PHASE_CLOCKS
+// Phase-clock build only: the first n counters of srnl_phase_buf (9 per
+// block of the last scan launch) into host memory. Returns a hipError_t.
+extern "C" int srnl_phase_clocks(unsigned long long *host, size_t n)
+{
+    return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(srnl_phase_buf),
+                                                n * sizeof(unsigned long long)));
+}
+#endif
