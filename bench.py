@@ -699,6 +699,10 @@ def main_bwd(args, wl_name):
 
 
 PHASES = ("load", "generation", "epilogue", "window_tables", "update", "readout", "refresh")
+BWD_PHASES = ("chunk_start_loads", "commit", "generation", "scalars", "forward_tables",
+              "backward_tables", "gin_recurrence", "token_products", "token_dots_tables",
+              "token_dq_dk", "scalar_chain", "generation_backward", "chunk_start_refresh")
+PHASE_SLOTS = 15
 
 
 def main_phase_clocks(args):
@@ -721,6 +725,13 @@ def main_phase_clocks(args):
     L.srnl_phase_clocks.restype = ctypes.c_int
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    def read_clocks(nch):
+        nb = (nch + 7) // 8 * 8
+        buf = np.zeros(nb * PHASE_SLOTS, dtype=np.uint64)
+        assert L.srnl_phase_clocks(buf.ctypes.data, buf.size) == 0
+        return buf.reshape(nb, PHASE_SLOTS)[:nch].astype(np.float64)
+
     sweep = synth.hier_sweep()
     wls = [synth.hier56(), synth.hier56(B=32), synth.dense200x304(), sweep[1], sweep[2],
            sweep[3], synth.plain14()]
@@ -731,19 +742,34 @@ def main_phase_clocks(args):
         for _ in range(3):
             srnl.scan_fwd(x, st, wl.heads, wl.d, 15, out=y)
         torch.cuda.synchronize()
-        nch = 4 * wl.B * wl.heads
-        nb = (nch + 7) // 8 * 8
-        buf = np.zeros(nb * 9, dtype=np.uint64)
-        assert L.srnl_phase_clocks(buf.ctypes.data, buf.size) == 0
-        a = buf.reshape(nb, 9)[:nch].astype(np.float64)
-        nsub = float(a[:, 7].mean())
+        a = read_clocks(4 * wl.B * wl.heads)
+        nsub = float(a[:, PHASE_SLOTS - 2].mean())
         rec = {"workload": wl.name, "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C,
-               "heads": wl.heads, "d": wl.d, "chains": nch, "sub_blocks_per_chain": nsub,
-               "cycles_per_chain": float(a[:, 8].mean()),
+               "heads": wl.heads, "d": wl.d, "chains": a.shape[0], "sub_blocks_per_chain": nsub,
+               "cycles_per_chain": float(a[:, PHASE_SLOTS - 1].mean()),
                "cycles_per_sub_block": {k: float(v) for k, v in
-                                        zip(PHASES, a[:, :7].mean(axis=0) / nsub)}}
+                                        zip(PHASES, a[:, :len(PHASES)].mean(axis=0) / nsub)}}
         print(json.dumps(rec), flush=True)
         del x, y
+    # the windowed backward of hier56 (its clocks overwrite those of the
+    # recording forward that srnl_scan_bwd launches first)
+    wl = synth.hier56()
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    st = torch.from_numpy(wl.states).to(dev)
+    y = srnl.scan_fwd(x, st, wl.heads, wl.d, 15)
+    dy = torch.from_numpy(np.random.default_rng(0).standard_normal(
+        tuple(y.shape)).astype(np.float32)).to(dev)
+    for _ in range(3):
+        srnl.scan_bwd(x, st, wl.heads, wl.d, dy, 15)
+    torch.cuda.synchronize()
+    a = read_clocks(4 * wl.B * wl.heads)
+    nwin = float(a[:, PHASE_SLOTS - 2].mean())
+    rec = {"workload": wl.name + "_bwd", "B": wl.B, "H": wl.H, "W": wl.W, "C": wl.C,
+           "heads": wl.heads, "d": wl.d, "chains": a.shape[0], "windows_per_chain": nwin,
+           "cycles_per_chain": float(a[:, PHASE_SLOTS - 1].mean()),
+           "cycles_per_window": {k: float(v) for k, v in
+                                 zip(BWD_PHASES, a[:, :len(BWD_PHASES)].mean(axis=0) / nwin)}}
+    print(json.dumps(rec), flush=True)
 
 
 def main():

@@ -742,16 +742,22 @@ constexpr int SCB_SERIES = 1, SCB_HARD = 2, SCB_CLAMP = 4;
 
 // Phase clocks (a separate build with -DSRNL_PHASE_CLOCKS=1, never the
 // library itself): wave 0 of every scan block reads the shader clock right
-// after each phase's closing barrier and accumulates the cycles per phase,
-// load, generation, epilogue, window tables, update, readout, refresh, in
-// srnl_phase_buf[block][0..6], then the sub-block count [7] and the whole
-// block's cycles [8]; srnl_phase_clocks copies them out.
+// after each phase's closing barrier and accumulates the cycles per phase in
+// srnl_phase_buf[block][0 .. kPhaseSlots - 3], then the count of sub-blocks
+// (windows in the backward) [kPhaseSlots - 2] and the whole block's cycles
+// [kPhaseSlots - 1]; srnl_phase_clocks copies them out. The forward scan's
+// phases: load, generation, epilogue, window tables, update, readout,
+// refresh. The windowed backward's: chunk start (loads), commit, generation,
+// transition scalars, forward tables, backward tables, the Gin recurrence,
+// the per-token gradients in three parts (products; row dots and tables;
+// dalpha, z, dq, dk), scalar chain, generation backward, chunk start
+// (refresh terms).
 #ifndef SRNL_PHASE_CLOCKS
 #define SRNL_PHASE_CLOCKS 0
 #endif
 #if SRNL_PHASE_CLOCKS
-constexpr int kPhaseBlocks = 16384;
-__device__ unsigned long long srnl_phase_buf[kPhaseBlocks * 9];
+constexpr int kPhaseBlocks = 16384, kPhaseSlots = 15;
+__device__ unsigned long long srnl_phase_buf[kPhaseBlocks * kPhaseSlots];
 #define SRNL_PHASE(k)                                                                \
     do {                                                                             \
         if (wave == 0) {                                                             \
@@ -1534,10 +1540,11 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     }
 #if SRNL_PHASE_CLOCKS
     if (wave == 0 && lane == 0 && blockIdx.x < kPhaseBlocks) {
-        for (int k = 0; k < 7; ++k)
-            srnl_phase_buf[blockIdx.x * 9 + k] = ph_acc[k];
-        srnl_phase_buf[blockIdx.x * 9 + 7] = ph_n;
-        srnl_phase_buf[blockIdx.x * 9 + 8] = clock64() - ph_t0;
+        unsigned long long *o = srnl_phase_buf + blockIdx.x * kPhaseSlots;
+        for (int k = 0; k < kPhaseSlots - 2; ++k)
+            o[k] = (k < 7) ? ph_acc[k] : 0;
+        o[kPhaseSlots - 2] = ph_n;
+        o[kPhaseSlots - 1] = clock64() - ph_t0;
     }
 #endif
 }
@@ -2728,8 +2735,9 @@ srnl_status srnl_init_states(float *states, int heads, int d, unsigned long long
 }  // extern "C"
 
 #if SRNL_PHASE_CLOCKS
-// Phase-clock build only: the first n counters of srnl_phase_buf (9 per
-// block of the last scan launch) into host memory. Returns a hipError_t.
+// Phase-clock build only: the first n counters of srnl_phase_buf
+// (kPhaseSlots per block of the last instrumented launch) into host memory.
+// Returns a hipError_t.
 extern "C" int srnl_phase_clocks(unsigned long long *host, size_t n)
 {
     return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(srnl_phase_buf),
