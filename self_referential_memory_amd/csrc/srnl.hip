@@ -1315,6 +1315,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     exchanging the halves through LDS (double-buffered by window
         //     parity: one barrier per window); Z is left as two partial sums
         //     (each wave also takes half of the N U terms) that the readout adds.
+        const bool first_sub = (s0 == c0);   // this sub-block opens its chunk
         if (wave < CW) {
             // the window chain is the chunk's critical path: with the long
             // sub-blocks (two chains a CU) its waves issue ahead of the
@@ -1344,10 +1345,24 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 if constexpr (SAVE)
                     save_q(svc + sl.o_q0(c0 / L, (s0 - c0) / 16 + win));
                 v4f A = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
+                // a chunk's first window opens from Q_0 = I: A is then the
+                // window's k^ rows (already complete, no exchange) and the z
+                // partial its q rows, in the column part that holds this
+                // wave's rows (the products give the same values exactly)
+                const bool q_id = first_sub && win == 0;
+                if (q_id) {
+                    const bool own = (it / NJ == jg);
 #pragma unroll
-                for (int jl = 0; jl < NJ; ++jl) {
-                    A = mfma16(kv[jl], qacc[jl], A);
-                    Z = mfma16(qv[jl], qacc[jl], Z);
+                    for (int i = 0; i < 4; ++i) {
+                        A[i] = KHa[ix(tb + 4 * lk + i, 16 * it + lm)];
+                        Z[i] = own ? QR[ix(tb + 4 * lk + i, 16 * it + lm)] : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int jl = 0; jl < NJ; ++jl) {
+                        A = mfma16(kv[jl], qacc[jl], A);
+                        Z = mfma16(qv[jl], qacc[jl], Z);
+                    }
                 }
                 const float4 ga = ld4(GA + tb + 4 * lk);
                 const float4 gz = ld4(GZ + tb + 4 * lk);
@@ -1367,7 +1382,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                                          KHa[ix(tb + 4 * lk + 2, 16 * jt + lm)] * rb.z,
                                          KHa[ix(tb + 4 * lk + 3, 16 * jt + lm)] * rb.w);
                 }
-                if (JS == 2) {
+                if (JS == 2 && !q_id) {
                     float *xb = XB + ((win & 1) * NTC + it) * 512 + 4 * lane;
                     st4(xb + 256 * jg, A[0], A[1], A[2], A[3]);
                     __syncthreads();
@@ -1430,7 +1445,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             // the update's per-window block barrier, for the waves outside it
             // (their MFMA work here would share the update waves' pipes and
             // lengthen the window chain)
-            for (int win = 0; win < nwin; ++win)
+            for (int win = first_sub ? 1 : 0; win < nwin; ++win)
                 __syncthreads();
         }
         __syncthreads();
