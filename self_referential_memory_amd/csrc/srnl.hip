@@ -905,6 +905,13 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     // after the window's table reads, so Q_L^T can be staged at the end of the
     // update, over the tables, when it does not cover rows the readout reads.
     constexpr bool QT_EARLY = JS == 2 && !Cfg::QT_IN_TOK;
+    // Single-window chunks at d = 64 (16-token sub-blocks: every sub-block
+    // a whole chunk of at most 16 tokens, opening from Q_0 = I): the refresh
+    // takes B Q_L = G_15 B + (B U^T) diag(R[15]) K^ without forming Q_L, half
+    // the products of B Q_L. (At d = 32 the two forms take the same products,
+    // and the Q-form measured faster.)
+    constexpr bool DIRECT = D == 64 && T == 16;
+    static_assert(!DIRECT || (NWIN == 1 && JS == 1 && CW == NW && !SAVE), "direct refresh layout");
 
     const size_t out_row0 = (static_cast<size_t>(slot) * B + b) * N;
 
@@ -920,6 +927,89 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     const unsigned long long ph_t0 = ph_t;
 #endif
     const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
+    // The direct refresh of a single-window chunk (DIRECT):
+    //   B' = G_15 B + P diag(R[15]) K^,  P = B U^T  [row][token],
+    // with U staged over the query rows by the update. P is formed per
+    // 16-row tile as P^T (the product's output is then the next product's
+    // second operand as it stands), and B'^T tiles come out with four
+    // consecutive channels of one row per lane. Each wave owns whole row tiles
+    // of B, so only the vector rows' dots cross waves (through the z rows,
+    // read by the readout already).
+    auto direct_refresh = [&](bool frz) {
+        if constexpr (DIRECT) {
+            constexpr int RTM = 3 * D / 16, RTD = (RTM + NW - 1) / NW;
+            __syncthreads();   // the readout is done with B_c and the z rows; U is staged
+            v4f pt[RTD];
+#pragma unroll
+            for (int w = 0; w < RTD; ++w) {
+                const int tm = wave + NW * w;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                if (tm < RTM) {
+#pragma unroll
+                    for (int kb = 0; kb < NTC; ++kb)
+                        acc = mfma16(ld4(Xs + ix(lm, 16 * kb + 4 * lk)),
+                                     ld4(Bs + ix(16 * tm + lm, 16 * kb + 4 * lk)), acc);
+                }
+                pt[w] = acc;
+            }
+            // vector rows: p_v[s] = b_v . u_s, LPD lanes per dot
+            constexpr int LPD = NT / 32, CPL = D / LPD;
+            static_assert(LPD == 4 || LPD == 8, "a power-of-two group of lanes per dot");
+            static_assert(CPL % 4 == 0 && NT == 4 * D, "whole 16-byte blocks; two lanes per output");
+            {
+                const int o = tid / LPD, part = tid % LPD, v = o >> 4, sx = o & 15;
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < CPL / 4; ++k) {
+                    const int c = part * CPL + 4 * k;
+                    const float4 uu = ld4(Xs + ix(sx, c));
+                    const float4 bb = ld4(Bs + ix(3 * D + v, c));
+                    acc = fmaf(uu.x, bb.x, acc);
+                    acc = fmaf(uu.y, bb.y, acc);
+                    acc = fmaf(uu.z, bb.z, acc);
+                    acc = fmaf(uu.w, bb.w, acc);
+                }
+                acc = group_sum<LPD>(acc);
+                if (part == 0)
+                    KZ[o] = acc;
+            }
+            __syncthreads();
+            const float g15 = WG[0];
+            const float4 rb = ld4(RB + 4 * lk);
+#pragma unroll
+            for (int w = 0; w < RTD; ++w) {
+                const int tm = wave + NW * w;
+                if (tm >= RTM || (frz && tm >= NTC))
+                    continue;
+                const float4 pb = make_float4(pt[w][0], pt[w][1], pt[w][2], pt[w][3]);
+#pragma unroll
+                for (int tn = 0; tn < NTC; ++tn) {
+                    float *bp = Bs + ix(16 * tm + lm, 16 * tn + 4 * lk);
+                    const float4 b0 = ld4(bp);
+                    v4f acc = {g15 * b0.x, g15 * b0.y, g15 * b0.z, g15 * b0.w};
+                    const int cc = 16 * tn + lm;
+                    const float4 ka = make_float4(rb.x * KHa[ix(4 * lk, cc)], rb.y * KHa[ix(4 * lk + 1, cc)],
+                                                  rb.z * KHa[ix(4 * lk + 2, cc)], rb.w * KHa[ix(4 * lk + 3, cc)]);
+                    acc = mfma16(ka, pb, acc);
+                    st4(bp, acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+            // vector rows: b_v' = G_15 b_v + sum_s p_v[s] R[15][s] k^_s, two
+            // lanes per element
+            if (!frz) {
+                const int o = tid >> 1, part = tid & 1, v = o / D, cc = o % D;
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int sx = 8 * part + k;
+                    acc = fmaf(KZ[16 * v + sx] * RB[sx], KHa[ix(sx, cc)], acc);
+                }
+                acc = group_sum<2>(acc);
+                if (part == 0)
+                    Bs[ix(3 * D + v, cc)] = fmaf(g15, Bs[ix(3 * D + v, cc)], acc);
+            }
+        }
+    };
     // Readout Y^T = B_c Z^T of token tile tm, channel tile tn: each lane ends
     // with four consecutive channels of one token (a 16-byte store).
     auto readout_tile = [&](int tm, int tn) {
@@ -1419,10 +1509,20 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     Z = mfma4(nnv.z, U[2], Z);
                     Z = mfma4(nnv.w, U[3], Z);
                 }
+                if constexpr (DIRECT) {
+                    // the u rows, [token][channel], over the query rows: this
+                    // lane has read its own elements of those (the z
+                    // partial above) and no other wave reads them
 #pragma unroll
-                for (int jl = 0; jl < NJ; ++jl) {
-                    qacc[jl] *= wg;
-                    qacc[jl] = mfma16(kt[jl], U, qacc[jl]);
+                    for (int rr = 0; rr < 4; ++rr)
+                        Xs[ix(4 * lk + rr, 16 * it + lm)] = U[rr];
+                }
+                if constexpr (!DIRECT || SAVE) {
+#pragma unroll
+                    for (int jl = 0; jl < NJ; ++jl) {
+                        qacc[jl] *= wg;
+                        qacc[jl] = mfma16(kt[jl], U, qacc[jl]);
+                    }
                 }
                 if (win + 1 < nwin)
                     load_rows(tb + 16);
@@ -1480,65 +1580,69 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 // (7) refresh the boundary: B <- B Q_L (tiles split over the
                 //     waves). Q_L^T is staged already unless it covers the z
                 //     rows, which the readout above had to finish with first.
-                if constexpr (Cfg::QT_IN_TOK) {
-                    __syncthreads();
-                    if (wave < CW)
-                        stage_qt();
-                    __syncthreads();
-                }
                 // frozen key/value and dynamics memories: only the M_c
                 // tiles (rows < D) and no vector memory are stored back
                 const bool frz = (flags & F_FREEZE_KV) != 0;
-                v4f racc[RTW];
-#pragma unroll
-                for (int w = 0; w < RTW; ++w) {
-                    const int tile = wave + w * NW;
-                    if (RT % NW != 0 && tile >= RT)
-                        break;
-                    const int tm = tile / NTC, tn = tile % NTC;
-                    float a[KS], bq[KS];
-                    ldrow(Bs, tm * 16 + lm, lk * KS, a);
-                    ldrow(Qt, tn * 16 + lm, lk * KS, bq);
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        acc = mfma4(a[s], bq[s], acc);
-                    racc[w] = acc;
-                }
-                // vector memories: two lanes per output element, each over
-                // half of the reduction index, summed by DPP (the same order
-                // in every sub-block configuration)
-                constexpr int VG = 2;
-                float vacc = 0.f;
-                const int vo = tid / VG, vpart = tid % VG;
-                const int vv = vo / D, vj = vo % D;
-                if (tid < 2 * D * VG && !frz) {
-#pragma unroll
-                    for (int k = 0; k < D / (4 * VG); ++k) {
-                        const int c = 4 * (vpart * (D / (4 * VG)) + k);
-                        const float4 bb = ld4(Bs + ix(3 * D + vv, c));
-                        const float4 qq = ld4(Qt + ix(vj, c));
-                        vacc = fmaf(bb.x, qq.x, vacc);
-                        vacc = fmaf(bb.y, qq.y, vacc);
-                        vacc = fmaf(bb.z, qq.z, vacc);
-                        vacc = fmaf(bb.w, qq.w, vacc);
+                if constexpr (DIRECT) {
+                    direct_refresh(frz);
+                } else {
+                    if constexpr (Cfg::QT_IN_TOK) {
+                        __syncthreads();
+                        if (wave < CW)
+                            stage_qt();
+                        __syncthreads();
                     }
-                    vacc = group_sum<VG>(vacc);
-                }
-                __syncthreads();
+                    v4f racc[RTW];
 #pragma unroll
-                for (int w = 0; w < RTW; ++w) {
-                    const int tile = wave + w * NW;
-                    if (RT % NW != 0 && tile >= RT)
-                        break;
-                    const int tm = tile / NTC, tn = tile % NTC;
+                    for (int w = 0; w < RTW; ++w) {
+                        const int tile = wave + w * NW;
+                        if (RT % NW != 0 && tile >= RT)
+                            break;
+                        const int tm = tile / NTC, tn = tile % NTC;
+                        float a[KS], bq[KS];
+                        ldrow(Bs, tm * 16 + lm, lk * KS, a);
+                        ldrow(Qt, tn * 16 + lm, lk * KS, bq);
+                        v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        if (!frz || tm < NTC)
-                            Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
+                        for (int s = 0; s < KS; ++s)
+                            acc = mfma4(a[s], bq[s], acc);
+                        racc[w] = acc;
+                    }
+                    // vector memories: two lanes per output element, each over
+                    // half of the reduction index, summed by DPP (the same order
+                    // in every sub-block configuration)
+                    constexpr int VG = 2;
+                    float vacc = 0.f;
+                    const int vo = tid / VG, vpart = tid % VG;
+                    const int vv = vo / D, vj = vo % D;
+                    if (tid < 2 * D * VG && !frz) {
+#pragma unroll
+                        for (int k = 0; k < D / (4 * VG); ++k) {
+                            const int c = 4 * (vpart * (D / (4 * VG)) + k);
+                            const float4 bb = ld4(Bs + ix(3 * D + vv, c));
+                            const float4 qq = ld4(Qt + ix(vj, c));
+                            vacc = fmaf(bb.x, qq.x, vacc);
+                            vacc = fmaf(bb.y, qq.y, vacc);
+                            vacc = fmaf(bb.z, qq.z, vacc);
+                            vacc = fmaf(bb.w, qq.w, vacc);
+                        }
+                        vacc = group_sum<VG>(vacc);
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int w = 0; w < RTW; ++w) {
+                        const int tile = wave + w * NW;
+                        if (RT % NW != 0 && tile >= RT)
+                            break;
+                        const int tm = tile / NTC, tn = tile % NTC;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            if (!frz || tm < NTC)
+                                Bs[ix(tm * 16 + 4 * lk + rr, tn * 16 + lm)] = racc[w][rr];
+                    }
+                    if (tid < 2 * D * VG && vpart == 0 && !frz)
+                        Bs[ix(3 * D + vv, vj)] = vacc;
                 }
-                if (tid < 2 * D * VG && vpart == 0 && !frz)
-                    Bs[ix(3 * D + vv, vj)] = vacc;
             }
             reset_q();
         }
