@@ -933,18 +933,18 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     // 16-row tile as P^T (the product's output is then the next product's
     // second operand as it stands), and B'^T tiles come out with four
     // consecutive channels of one row per lane. Each wave owns whole row tiles
-    // of B, so only the vector rows' dots cross waves (through the z rows,
-    // read by the readout already).
-    auto direct_refresh = [&](bool frz) {
+    // of B. The first part reads only B_c, U and k^, so it runs beside the
+    // readout; the vector rows' dots cross waves through the v rows (dead
+    // after the update). The second part writes B' after a barrier.
+    constexpr int RTM_D = 3 * D / 16, RTD_D = (RTM_D + NW - 1) / NW;
+    float *const PV = Es;
+    auto direct_products = [&](v4f (&pt)[RTD_D]) {
         if constexpr (DIRECT) {
-            constexpr int RTM = 3 * D / 16, RTD = (RTM + NW - 1) / NW;
-            __syncthreads();   // the readout is done with B_c and the z rows; U is staged
-            v4f pt[RTD];
 #pragma unroll
-            for (int w = 0; w < RTD; ++w) {
+            for (int w = 0; w < RTD_D; ++w) {
                 const int tm = wave + NW * w;
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
-                if (tm < RTM) {
+                if (tm < RTM_D) {
 #pragma unroll
                     for (int kb = 0; kb < NTC; ++kb)
                         acc = mfma16(ld4(Xs + ix(lm, 16 * kb + 4 * lk)),
@@ -956,41 +956,42 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             constexpr int LPD = NT / 32, CPL = D / LPD;
             static_assert(LPD == 4 || LPD == 8, "a power-of-two group of lanes per dot");
             static_assert(CPL % 4 == 0 && NT == 4 * D, "whole 16-byte blocks; two lanes per output");
-            {
-                const int o = tid / LPD, part = tid % LPD, v = o >> 4, sx = o & 15;
-                float acc = 0.f;
+            const int o = tid / LPD, part = tid % LPD, v = o >> 4, sx = o & 15;
+            float acc = 0.f;
 #pragma unroll
-                for (int k = 0; k < CPL / 4; ++k) {
-                    const int c = part * CPL + 4 * k;
-                    const float4 uu = ld4(Xs + ix(sx, c));
-                    const float4 bb = ld4(Bs + ix(3 * D + v, c));
-                    acc = fmaf(uu.x, bb.x, acc);
-                    acc = fmaf(uu.y, bb.y, acc);
-                    acc = fmaf(uu.z, bb.z, acc);
-                    acc = fmaf(uu.w, bb.w, acc);
-                }
-                acc = group_sum<LPD>(acc);
-                if (part == 0)
-                    KZ[o] = acc;
+            for (int k = 0; k < CPL / 4; ++k) {
+                const int c = part * CPL + 4 * k;
+                const float4 uu = ld4(Xs + ix(sx, c));
+                const float4 bb = ld4(Bs + ix(3 * D + v, c));
+                acc = fmaf(uu.x, bb.x, acc);
+                acc = fmaf(uu.y, bb.y, acc);
+                acc = fmaf(uu.z, bb.z, acc);
+                acc = fmaf(uu.w, bb.w, acc);
             }
-            __syncthreads();
+            acc = group_sum<LPD>(acc);
+            if (part == 0)
+                PV[o] = acc;
+        }
+    };
+    auto direct_store = [&](const v4f (&pt)[RTD_D], bool frz) {
+        if constexpr (DIRECT) {
+            __syncthreads();   // the readout is done with B_c; the vector-row dots are in
             const float g15 = WG[0];
             const float4 rb = ld4(RB + 4 * lk);
 #pragma unroll
-            for (int w = 0; w < RTD; ++w) {
-                const int tm = wave + NW * w;
-                if (tm >= RTM || (frz && tm >= NTC))
-                    continue;
-                const float4 pb = make_float4(pt[w][0], pt[w][1], pt[w][2], pt[w][3]);
+            for (int tn = 0; tn < NTC; ++tn) {
+                const int cc = 16 * tn + lm;
+                const float4 ka = make_float4(rb.x * KHa[ix(4 * lk, cc)], rb.y * KHa[ix(4 * lk + 1, cc)],
+                                              rb.z * KHa[ix(4 * lk + 2, cc)], rb.w * KHa[ix(4 * lk + 3, cc)]);
 #pragma unroll
-                for (int tn = 0; tn < NTC; ++tn) {
+                for (int w = 0; w < RTD_D; ++w) {
+                    const int tm = wave + NW * w;
+                    if (tm >= RTM_D || (frz && tm >= NTC))
+                        continue;
                     float *bp = Bs + ix(16 * tm + lm, 16 * tn + 4 * lk);
                     const float4 b0 = ld4(bp);
                     v4f acc = {g15 * b0.x, g15 * b0.y, g15 * b0.z, g15 * b0.w};
-                    const int cc = 16 * tn + lm;
-                    const float4 ka = make_float4(rb.x * KHa[ix(4 * lk, cc)], rb.y * KHa[ix(4 * lk + 1, cc)],
-                                                  rb.z * KHa[ix(4 * lk + 2, cc)], rb.w * KHa[ix(4 * lk + 3, cc)]);
-                    acc = mfma16(ka, pb, acc);
+                    acc = mfma16(ka, make_float4(pt[w][0], pt[w][1], pt[w][2], pt[w][3]), acc);
                     st4(bp, acc[0], acc[1], acc[2], acc[3]);
                 }
             }
@@ -1002,7 +1003,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int sx = 8 * part + k;
-                    acc = fmaf(KZ[16 * v + sx] * RB[sx], KHa[ix(sx, cc)], acc);
+                    acc = fmaf(PV[16 * v + sx] * RB[sx], KHa[ix(sx, cc)], acc);
                 }
                 acc = group_sum<2>(acc);
                 if (part == 0)
@@ -1573,6 +1574,11 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 for (int tn = tn0; tn < NTC; tn += tns)
                     readout_tile(tm, tn);
         }
+        v4f pt_d[RTD_D];
+        if constexpr (DIRECT) {
+            if (chunk_end && cend < N)
+                direct_products(pt_d);
+        }
 
         SRNL_PHASE(5);
         if (chunk_end) {
@@ -1584,7 +1590,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 // tiles (rows < D) and no vector memory are stored back
                 const bool frz = (flags & F_FREEZE_KV) != 0;
                 if constexpr (DIRECT) {
-                    direct_refresh(frz);
+                    direct_store(pt_d, frz);
                 } else {
                     if constexpr (Cfg::QT_IN_TOK) {
                         __syncthreads();
