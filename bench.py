@@ -699,8 +699,8 @@ def main_bwd(args, wl_name):
 
 
 PHASES = ("load", "generation", "epilogue", "window_tables", "update", "readout", "refresh")
-BWD_PHASES = ("chunk_start_loads", "commit", "generation_and_scalars", "unused", "forward_tables",
-              "backward_tables", "gin_recurrence", "token_products", "token_dots_tables",
+BWD_PHASES = ("chunk_start_loads", "commit", "dz_and_tables", "unused", "dz_u_and_lf_nf_u",
+              "unused", "gin_recurrence", "token_products", "token_dots_tables",
               "token_dq_dk", "scalar_chain", "generation_backward", "chunk_start_refresh")
 PHASE_SLOTS = 15
 

@@ -236,8 +236,8 @@ srnl_status srnl_fuse(const float *y_routes, int B, int H, int W, int C,
  *   dy      [R][B][H*W][C] fp32 in the layout srnl_scan_fwd writes.
  * At d = 32 with the readout after the write, a recording forward writes,
  * per chain, every chunk's boundary and closing state and every 16-token
- * window's opening state, update rows and transition scalars into the
- * workspace; the adjoint then walks the chunks and windows backwards, 16
+ * window's opening state, update rows, transition scalars and window tables
+ * into the workspace; the adjoint then walks the chunks and windows backwards, 16
  * tokens at a time. With SRNL_FLAG_RECORD the record comes instead from
  * params->workspace, written by srnl_scan_fwd with the same arguments and
  * params, and the workspace here holds only the rest (smaller

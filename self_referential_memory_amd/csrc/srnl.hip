@@ -709,10 +709,14 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
 
 // Per-chain record of the forward that the windowed backward reads (SAVE):
 // every chunk's boundary rows and closing Q_L, and every 16-token window's
-// opening Q_0, its u_t rows and its tokens' transition scalars (windows
-// counted from each chunk start). Scalars of a token, 16 floats: 1/sqrt(|k|^2
-// + eps), |k^|^2, |e|^2, g, eta, alpha, 1 - alpha, u = eta g / (1 - alpha),
-// eta', eta'', the branch bits (SCB_*), b_eta . x, b_alpha . x, 3 unused.
+// opening Q_0, its u_t rows, its tokens' transition scalars and its window
+// tables (windows counted from each chunk start). Scalars of a token, 16
+// floats: 1/sqrt(|k|^2 + eps), |k^|^2, |e|^2, g, eta, alpha, 1 - alpha,
+// u = eta g / (1 - alpha), eta', eta'', the branch bits (SCB_*), b_eta . x,
+// b_alpha . x, 3 unused. Window tables (TW_* offsets, TW floats): the k^ and
+// e rows [16][D] (zero on padding tokens), the Grams k^_s . k^_t and
+// q_t . k^_s and R[t][s] (masked: 1 on the diagonal, 0 above), each [t][s],
+// T = (I + L)^-1 transposed ([s][t]), then G_t, G_{t-1} and R[15][s].
 // Chains are chain_floats apart; inside a chain the layout depends on the
 // route's chunk count nch and window slots per chunk nwc.
 struct FwdSave {
@@ -721,6 +725,9 @@ struct FwdSave {
 };
 template <int D> struct SaveLayout {
     static constexpr long long BR = (3LL * D + 2) * D;   // boundary rows
+    static constexpr int TW_KH = 0, TW_E = 16 * D, TW_KK = 32 * D, TW_QK = TW_KK + 256,
+                         TW_R = TW_QK + 256, TW_T = TW_R + 256, TW_G = TW_T + 256,
+                         TW_GP = TW_G + 16, TW_PI = TW_GP + 16, TW = TW_PI + 16 + 16;
     long long nch, nwc;
     __host__ __device__ long long o_bnd(long long c) const { return c * BR; }
     __host__ __device__ long long o_ql(long long c) const { return nch * BR + c * D * D; }
@@ -733,8 +740,11 @@ template <int D> struct SaveLayout {
     __host__ __device__ long long o_sc(long long c, long long w) const {
         return nch * (BR + D * D) + nch * nwc * (D * D + 16 * D) + (c * nwc + w) * 256;
     }
+    __host__ __device__ long long o_tab(long long c, long long w) const {
+        return nch * (BR + D * D) + nch * nwc * (D * D + 16 * D + 256) + (c * nwc + w) * TW;
+    }
     __host__ __device__ long long floats() const {
-        return nch * (BR + D * D + nwc * (D * D + 16 * D + 256));
+        return nch * (BR + D * D + nwc * (D * D + 16 * D + 256 + TW));
     }
 };
 // branch bits of a recorded token: soft-cap series, hard cap taken, clamp taken
@@ -1234,6 +1244,14 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     EH[u] = eta2;
                 }
                 if constexpr (SAVE) {
+                    float *tw = svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + u / 16) + (u % 16) * D + c0e;
+#pragma unroll
+                    for (int c4 = 0; c4 < ECPL / 4; ++c4) {
+                        st4(tw + SaveLayout<D>::TW_KH + 4 * c4, khv[4 * c4], khv[4 * c4 + 1],
+                            khv[4 * c4 + 2], khv[4 * c4 + 3]);
+                        st4(tw + SaveLayout<D>::TW_E + 4 * c4, evv[4 * c4], evv[4 * c4 + 1],
+                            evv[4 * c4 + 2], evv[4 * c4 + 3]);
+                    }
                     if (ep == 0) {
                         float4 *ds = reinterpret_cast<float4 *>(
                             svc + sl.o_sc(c0 / L, (s0 - c0) / 16 + u / 16) + (u % 16) * 16);
@@ -1248,6 +1266,18 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                 for (int c4 = 0; c4 < ECPL / 4; ++c4)
                     st4(KHa + ix(u, c0e + 4 * c4), 0.f, 0.f, 0.f, 0.f);
+                if constexpr (SAVE) {
+                    // (only inside the sub-block's windows: past them lie the
+                    // next chunk's slots)
+                    if (u / 16 < nwin) {
+                        float *tw = svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + u / 16) + (u % 16) * D + c0e;
+#pragma unroll
+                        for (int c4 = 0; c4 < ECPL / 4; ++c4) {
+                            st4(tw + SaveLayout<D>::TW_KH + 4 * c4, 0.f, 0.f, 0.f, 0.f);
+                            st4(tw + SaveLayout<D>::TW_E + 4 * c4, 0.f, 0.f, 0.f, 0.f);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int c = 0; c < ECPL; ++c)
                     Et[(c0e + c) * ETS + et_col(c0e + c, u)] = 0.f;
@@ -1333,6 +1363,20 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             }
             st4(lc + t * WS + 4 * lk, Lr[0], Lr[1], Lr[2], Lr[3]);
             st4(Nn + win * Cfg::WSTR_N + t * NS + 4 * lk, Nr[0], Nr[1], Nr[2], Nr[3]);
+            if constexpr (SAVE) {
+                using SL = SaveLayout<D>;
+                float *tw = svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + win) + t * 16 + 4 * lk;
+                st4(tw + SL::TW_KK, gkk[0], gkk[1], gkk[2], gkk[3]);
+                st4(tw + SL::TW_QK, gqk[0], gqk[1], gqk[2], gqk[3]);
+                st4(tw + SL::TW_R, Rr[0], Rr[1], Rr[2], Rr[3]);
+                float *tg = svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + win);
+                if (lk == 0) {
+                    tg[SL::TW_G + t] = pi;
+                    tg[SL::TW_GP + t] = gprev;
+                }
+                if (t == 15)
+                    st4(tg + SL::TW_PI + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
+            }
             if (t == 15)
                 st4(RB + tb + 4 * lk, Rr[0], Rr[1], Rr[2], Rr[3]);
             if (lk == 0) {
@@ -1384,6 +1428,9 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                                 acc[i] = fmaf(-lrow[i][4 * bb + j], xb[j], acc[i]);
                     }
                 }
+                if constexpr (SAVE)   // T transposed: [c][4 g + i]
+                    st4(svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + win) + SaveLayout<D>::TW_T + c * 16 + 4 * g,
+                        xf[0], xf[1], xf[2], xf[3]);
                 const float ec = -EH[tb + c];
                 float *tp = Tp + win * Cfg::WSTR_T;
 #pragma unroll
