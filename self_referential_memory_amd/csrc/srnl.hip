@@ -1488,18 +1488,21 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 // partial its q rows, in the column part that holds this
                 // wave's rows (the products give the same values exactly)
                 const bool q_id = first_sub && win == 0;
+                // (without outputs, the record-only forward forms no z rows)
                 if (q_id) {
                     const bool own = (it / NJ == jg);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         A[i] = KHa[ix(tb + 4 * lk + i, 16 * it + lm)];
-                        Z[i] = own ? QR[ix(tb + 4 * lk + i, 16 * it + lm)] : 0.f;
+                        if constexpr (OUT)
+                            Z[i] = own ? QR[ix(tb + 4 * lk + i, 16 * it + lm)] : 0.f;
                     }
                 } else {
 #pragma unroll
                     for (int jl = 0; jl < NJ; ++jl) {
                         A = mfma16(kv[jl], qacc[jl], A);
-                        Z = mfma16(qv[jl], qacc[jl], Z);
+                        if constexpr (OUT)
+                            Z = mfma16(qv[jl], qacc[jl], Z);
                     }
                 }
                 const float4 ga = ld4(GA + tb + 4 * lk);
@@ -1544,18 +1547,20 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                             du[(4 * lk + rr) * D + 16 * it + lm] = U[rr];
                     }
                 }
-                Z[0] *= gz.x;
-                Z[1] *= gz.y;
-                Z[2] *= gz.z;
-                Z[3] *= gz.w;
-                if (JS == 1) {
-                    Z = mfma16(nnv, U, Z);
-                } else if (jg == 0) {
-                    Z = mfma4(nnv.x, U[0], Z);
-                    Z = mfma4(nnv.y, U[1], Z);
-                } else {
-                    Z = mfma4(nnv.z, U[2], Z);
-                    Z = mfma4(nnv.w, U[3], Z);
+                if constexpr (OUT) {
+                    Z[0] *= gz.x;
+                    Z[1] *= gz.y;
+                    Z[2] *= gz.z;
+                    Z[3] *= gz.w;
+                    if (JS == 1) {
+                        Z = mfma16(nnv, U, Z);
+                    } else if (jg == 0) {
+                        Z = mfma4(nnv.x, U[0], Z);
+                        Z = mfma4(nnv.y, U[1], Z);
+                    } else {
+                        Z = mfma4(nnv.z, U[2], Z);
+                        Z = mfma4(nnv.w, U[3], Z);
+                    }
                 }
                 if constexpr (DIRECT) {
                     // the u rows, [token][channel], over the query rows: this
@@ -1574,10 +1579,12 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 }
                 if (win + 1 < nwin)
                     load_rows(tb + 16);
-                float *zd = (JS == 2 && jg == 1) ? KZ2 : KZ;
+                if constexpr (OUT) {
+                    float *zd = (JS == 2 && jg == 1) ? KZ2 : KZ;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    zd[ix(tb + 4 * lk + i, 16 * it + lm)] = Z[i];
+                    for (int i = 0; i < 4; ++i)
+                        zd[ix(tb + 4 * lk + i, 16 * it + lm)] = Z[i];
+                }
             }
             if constexpr (T >= 64)
                 __builtin_amdgcn_s_setprio(0);
