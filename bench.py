@@ -699,7 +699,7 @@ def main_bwd(args, wl_name):
 
 
 PHASES = ("load", "generation", "epilogue", "window_tables", "update", "readout", "refresh")
-BWD_PHASES = ("chunk_start_loads", "commit", "dz_and_tables", "unused", "dz_u_and_lf_nf_u",
+BWD_PHASES = ("chunk_start_loads", "commit", "dz_and_tables", "unused", "unused",
               "unused", "gin_recurrence", "token_products", "token_dots_tables",
               "token_dq_dk", "scalar_chain", "generation_backward", "chunk_start_refresh")
 PHASE_SLOTS = 15

@@ -716,7 +716,8 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
 // b_alpha . x, 3 unused. Window tables (TW_* offsets, TW floats): the k^ and
 // e rows [16][D] (zero on padding tokens), the Grams k^_s . k^_t and
 // q_t . k^_s and R[t][s] (masked: 1 on the diagonal, 0 above), each [t][s],
-// T = (I + L)^-1 transposed ([s][t]), then G_t, G_{t-1} and R[15][s].
+// T = (I + L)^-1 transposed ([s][t]), R[t-1][s] (k^_s . k^_t) (s < t) and
+// R[t][s] (q_t . k^_s) (s <= t), each [t][s], then G_t, G_{t-1} and R[15][s].
 // Chains are chain_floats apart; inside a chain the layout depends on the
 // route's chunk count nch and window slots per chunk nwc.
 struct FwdSave {
@@ -726,8 +727,9 @@ struct FwdSave {
 template <int D> struct SaveLayout {
     static constexpr long long BR = (3LL * D + 2) * D;   // boundary rows
     static constexpr int TW_KH = 0, TW_E = 16 * D, TW_KK = 32 * D, TW_QK = TW_KK + 256,
-                         TW_R = TW_QK + 256, TW_T = TW_R + 256, TW_G = TW_T + 256,
-                         TW_GP = TW_G + 16, TW_PI = TW_GP + 16, TW = TW_PI + 16 + 16;
+                         TW_R = TW_QK + 256, TW_T = TW_R + 256, TW_LF = TW_T + 256,
+                         TW_NF = TW_LF + 256, TW_G = TW_NF + 256, TW_GP = TW_G + 16,
+                         TW_PI = TW_GP + 16, TW = TW_PI + 16 + 16;
     long long nch, nwc;
     __host__ __device__ long long o_bnd(long long c) const { return c * BR; }
     __host__ __device__ long long o_ql(long long c) const { return nch * BR + c * D * D; }
@@ -1369,6 +1371,12 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 st4(tw + SL::TW_KK, gkk[0], gkk[1], gkk[2], gkk[3]);
                 st4(tw + SL::TW_QK, gqk[0], gqk[1], gqk[2], gqk[3]);
                 st4(tw + SL::TW_R, Rr[0], Rr[1], Rr[2], Rr[3]);
+                float lf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lf[i] = (4 * lk + i < t) ? P[i] * gkk[i] : 0.0f;
+                st4(tw + SL::TW_LF, lf[0], lf[1], lf[2], lf[3]);
+                st4(tw + SL::TW_NF, Nr[0], Nr[1], Nr[2], Nr[3]);
                 float *tg = svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + win);
                 if (lk == 0) {
                     tg[SL::TW_G + t] = pi;
