@@ -712,8 +712,8 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
 // opening Q_0, its u_t rows, its tokens' transition scalars and its window
 // tables (windows counted from each chunk start). Scalars of a token, 16
 // floats: 1/sqrt(|k|^2 + eps), |k^|^2, |e|^2, g, eta, alpha, 1 - alpha,
-// u = eta g / (1 - alpha), eta', eta'', the branch bits (SCB_*), b_eta . x,
-// b_alpha . x, 3 unused. Window tables (TW_* offsets, TW floats): the k^ and
+// u = eta g / (1 - alpha), eta', eta'', the branch bits (SCB_*), and the five
+// coefficients of the backward through these scalars (written with them). Window tables (TW_* offsets, TW floats): the k^ and
 // e rows [16][D] (zero on padding tokens), the Grams k^_s . k^_t and
 // q_t . k^_s and R[t][s] (masked: 1 on the diagonal, 0 above), each [t][s],
 // T = (I + L)^-1 transposed ([s][t]), R[t-1][s] (k^_s . k^_t) (s < t) and
@@ -1255,12 +1255,56 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                             evv[4 * c4 + 2], evv[4 * c4 + 3]);
                     }
                     if (ep == 0) {
+                        // The backward through these scalars is linear in
+                        // dL/deta'' and dL/dalpha; its five coefficients:
+                        //   dL/d(eta pre-activation)   = c0 dL/deta''
+                        //   dL/d(alpha pre-activation) = c1 dL/dalpha + c2 dL/deta''
+                        //   dL/d|e|^2 = c3 dL/deta'',  dL/d|k^|^2 = c4 dL/deta''
+                        const bool clamp_on = (bits & SCB_CLAMP) != 0;
+                        const float p1 = clamp_on ? 0.f : 1.f;   // deta1 per deta''
+                        float ke = 0.f, km = 0.f, kg = 0.f;      // d eta, d m, d g per deta1
+                        if (flags & F_NO_CAP) {
+                            ke = 1.f;
+                        } else if (flags & F_HARD_CAP) {
+                            if (bits & SCB_HARD) {
+                                km = 1.0f / g;
+                                kg = -m / (g * g);
+                            } else {
+                                ke = 1.f;
+                            }
+                        } else if (g > 0.0f) {
+                            float kuu;
+                            if (bits & SCB_SERIES) {
+                                ke = 1.0f - uu * uu * (1.0f / 3.0f);
+                                kuu = eta * (-2.0f * uu * (1.0f / 3.0f));
+                            } else {
+                                const float th = tanhf(uu);
+                                km = th / g;
+                                kuu = m * (1.0f - th * th) / g;
+                                kg = -m * th / (g * g);
+                            }
+                            ke += kuu * g / m;
+                            kg += kuu * eta / m;
+                            km -= kuu * eta * g / (m * m);
+                        } else {
+                            ke = 1.f;
+                        }
+                        const float ga = (flags & F_FIXED_ALPHA) ? 0.f : alpha * (1.0f - alpha / alpha_max);
+                        const float cf0 = p1 * ke * eta * (1.0f - eta);
+                        const float cf2 = ga * ((clamp_on ? 2.0f / nkh2 : 0.f) - p1 * km);
+                        float cf3 = 0.f, cf4 = 0.f;
+                        if (g > 0.0f) {
+                            cf3 = p1 * kg * g / (2.0f * ne2);
+                            cf4 = p1 * kg * g / (2.0f * nkh2);
+                        }
+                        if (clamp_on)
+                            cf4 -= 2.0f * alpha / (nkh2 * nkh2);
                         float4 *ds = reinterpret_cast<float4 *>(
                             svc + sl.o_sc(c0 / L, (s0 - c0) / 16 + u / 16) + (u % 16) * 16);
                         ds[0] = make_float4(inv, nkh2, ne2, g);
                         ds[1] = make_float4(eta, alpha, m, uu);
-                        ds[2] = make_float4(eta1, eta2, __int_as_float(bits), er);
-                        ds[3] = make_float4(ar, 0.f, 0.f, 0.f);
+                        ds[2] = make_float4(eta1, eta2, __int_as_float(bits), cf0);
+                        ds[3] = make_float4(ga, cf2, cf3, cf4);
                     }
                 }
             } else {
