@@ -709,12 +709,13 @@ __device__ __forceinline__ float quad_bcast(float v, int src)
 
 // Per-chain record of the forward that the windowed backward reads (SAVE):
 // every chunk's boundary rows and closing Q_L, and every 16-token window's
-// opening Q_0, its u_t rows, its tokens' transition scalars and its window
-// tables (windows counted from each chunk start). Scalars of a token, 16
-// floats: 1/sqrt(|k|^2 + eps), |k^|^2, |e|^2, g, eta, alpha, 1 - alpha,
-// u = eta g / (1 - alpha), eta', eta'', the branch bits (SCB_*), and the five
-// coefficients of the backward through these scalars (written with them). Window tables (TW_* offsets, TW floats): the k^ and
-// e rows [16][D] (zero on padding tokens), the Grams k^_s . k^_t and
+// opening Q_0 (neither at d = 64, see SaveLayout), its u_t rows, its tokens'
+// transition scalars and its window tables (windows counted from each chunk
+// start). Scalars of a token, 16 floats: 1/sqrt(|k|^2 + eps), |k^|^2, |e|^2,
+// g, eta, alpha, 1 - alpha, u = eta g / (1 - alpha), eta', eta'', the branch
+// bits (SCB_*), and the five coefficients of the backward through these
+// scalars (written with them). Window tables (TW_* offsets, TW floats): the
+// k^ and e rows [16][D] (zero on padding tokens), the Grams k^_s . k^_t and
 // q_t . k^_s and R[t][s] (masked: 1 on the diagonal, 0 above), each [t][s],
 // T = (I + L)^-1 transposed ([s][t]), R[t-1][s] (k^_s . k^_t) (s < t) and
 // R[t][s] (q_t . k^_s) (s <= t), each [t][s], then G_t, G_{t-1} and R[15][s].
@@ -724,29 +725,35 @@ struct FwdSave {
     float *base = nullptr;
     long long chain_floats = 0;
 };
+// At d = 64 the record serves chunks of one window only: every window opens
+// its chunk (Q_0 = I) and the forward refreshes the boundary without forming
+// Q_L, so the record holds no Q_0 or Q_L there (the backward rebuilds Q_L
+// from the window's u and k^ rows).
 template <int D> struct SaveLayout {
     static constexpr long long BR = (3LL * D + 2) * D;   // boundary rows
+    static constexpr bool QREC = D != 64;                // Q_0 and Q_L recorded
+    static constexpr long long QD = QREC ? D * D : 0;
     static constexpr int TW_KH = 0, TW_E = 16 * D, TW_KK = 32 * D, TW_QK = TW_KK + 256,
                          TW_R = TW_QK + 256, TW_T = TW_R + 256, TW_LF = TW_T + 256,
                          TW_NF = TW_LF + 256, TW_G = TW_NF + 256, TW_GP = TW_G + 16,
                          TW_PI = TW_GP + 16, TW = TW_PI + 16 + 16;
     long long nch, nwc;
     __host__ __device__ long long o_bnd(long long c) const { return c * BR; }
-    __host__ __device__ long long o_ql(long long c) const { return nch * BR + c * D * D; }
+    __host__ __device__ long long o_ql(long long c) const { return nch * BR + c * QD; }
     __host__ __device__ long long o_q0(long long c, long long w) const {
-        return nch * (BR + D * D) + (c * nwc + w) * D * D;
+        return nch * (BR + QD) + (c * nwc + w) * QD;
     }
     __host__ __device__ long long o_u(long long c, long long w) const {
-        return nch * (BR + D * D) + nch * nwc * D * D + (c * nwc + w) * 16 * D;
+        return nch * (BR + QD) + nch * nwc * QD + (c * nwc + w) * 16 * D;
     }
     __host__ __device__ long long o_sc(long long c, long long w) const {
-        return nch * (BR + D * D) + nch * nwc * (D * D + 16 * D) + (c * nwc + w) * 256;
+        return nch * (BR + QD) + nch * nwc * (QD + 16 * D) + (c * nwc + w) * 256;
     }
     __host__ __device__ long long o_tab(long long c, long long w) const {
-        return nch * (BR + D * D) + nch * nwc * (D * D + 16 * D + 256) + (c * nwc + w) * TW;
+        return nch * (BR + QD) + nch * nwc * (QD + 16 * D + 256) + (c * nwc + w) * TW;
     }
     __host__ __device__ long long floats() const {
-        return nch * (BR + D * D + nwc * (D * D + 16 * D + 256 + TW));
+        return nch * (BR + QD + nwc * (QD + 16 * D + 256 + TW));
     }
 };
 // branch bits of a recorded token: soft-cap series, hard cap taken, clamp taken
@@ -923,7 +930,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
     // the products of B Q_L. (At d = 32 the two forms take the same products,
     // and the Q-form measured faster.)
     constexpr bool DIRECT = D == 64 && T == 16;
-    static_assert(!DIRECT || (NWIN == 1 && JS == 1 && CW == NW && !SAVE), "direct refresh layout");
+    static_assert(!DIRECT || (NWIN == 1 && JS == 1 && CW == NW), "direct refresh layout");
+    static_assert(!SAVE || SaveLayout<D>::QREC != DIRECT, "the record keeps Q_0 and Q_L unless direct");
 
     const size_t out_row0 = (static_cast<size_t>(slot) * B + b) * N;
 
@@ -1532,7 +1540,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             };
             for (int win = 0; win < nwin; ++win) {
                 const int tb = 16 * win;
-                if constexpr (SAVE)
+                if constexpr (SAVE && !DIRECT)
                     save_q(svc + sl.o_q0(c0 / L, (s0 - c0) / 16 + win));
                 v4f A = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
                 // a chunk's first window opens from Q_0 = I: A is then the
@@ -1622,7 +1630,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     for (int rr = 0; rr < 4; ++rr)
                         Xs[ix(4 * lk + rr, 16 * it + lm)] = U[rr];
                 }
-                if constexpr (!DIRECT || SAVE) {
+                if constexpr (!DIRECT) {
 #pragma unroll
                     for (int jl = 0; jl < NJ; ++jl) {
                         qacc[jl] *= wg;
@@ -1644,7 +1652,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 if (chunk_end && cend < N)
                     stage_qt();
             }
-            if constexpr (SAVE) {
+            if constexpr (SAVE && !DIRECT) {
                 if (chunk_end)
                     save_q(svc + sl.o_ql(c0 / L));
             }
@@ -1973,6 +1981,7 @@ __global__ __launch_bounds__(256) void init_kernel(float *__restrict__ st, long 
 
 #include "srnl_bwd.inc"
 #include "srnl_bwd_wy.inc"
+#include "srnl_bwd_wy64.inc"
 
 // ------------------------------------------------------------ host side
 
@@ -2118,10 +2127,11 @@ srnl_status launch_scan(const void *x, const srnl_params *p, int B, int H, int W
     }
 }
 
-// The recording forward at d = 32 (readout after the write): the record sv
-// of every chain for the windowed backward, and the route outputs when out
-// is not NULL. The sub-block follows the longest chunk.
-template <typename InT>
+// The recording forward (readout after the write; d = 32, or d = 64 with
+// chunks of at most 16 tokens): the record sv of every chain for the
+// windowed backward, and the route outputs when out is not NULL. The
+// sub-block follows the longest chunk.
+template <int D, typename InT>
 srnl_status launch_record_fwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
                               int heads, unsigned mask, float *out, const FwdSave &sv)
 {
@@ -2135,15 +2145,19 @@ srnl_status launch_record_fwd(const void *x, const srnl_params *p, int B, int H,
     auto go = [&](auto t, auto o) {
         constexpr int T = decltype(t)::value;
         constexpr bool O = decltype(o)::value;
-        launch_scan_mfma<32, T, InT, true, O>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out, sv);
+        launch_scan_mfma<D, T, InT, true, O>(x, p, B, H, W, C, heads, mask, R, nc, nblocks, out, sv);
     };
     auto pick = [&](auto o) {
-        if (L <= 16)
+        if constexpr (D == 64) {   // chunks of at most 16 tokens only
             go(std::integral_constant<int, 16>(), o);
-        else if (L <= 32)
-            go(std::integral_constant<int, 32>(), o);
-        else
-            go(std::integral_constant<int, 64>(), o);
+        } else {
+            if (L <= 16)
+                go(std::integral_constant<int, 16>(), o);
+            else if (L <= 32)
+                go(std::integral_constant<int, 32>(), o);
+            else
+                go(std::integral_constant<int, 64>(), o);
+        }
     };
     if (out)
         pick(std::true_type());
@@ -2191,13 +2205,25 @@ struct BwdLayout {
 
 long long align64(long long n) { return (n + 63) / 64 * 64; }
 
-// The windowed backward (d = 32, readout after the write) reads a record of
+// The windowed backward (readout after the write; d = 32, or d = 64 when no
+// active route's chunk is longer than one 16-token window) reads a record of
 // the forward instead of re-running it token by token.
-bool bwd_windowed(int d, const srnl_params *p) { return d == 32 && !(p->flags & F_READ_BEFORE); }
+bool bwd_windowed(int d, const srnl_params *p, int H, int W, unsigned mask)
+{
+    if (p->flags & F_READ_BEFORE)
+        return false;
+    return d == 32 || (d == 64 && longest_chunk(H, W, mask, p->chunk_row, p->chunk_col) <= 16);
+}
+
+// Floats of one chain's forward record for nch chunks of nwc window slots.
+long long record_floats(int d, long long nch, long long nwc)
+{
+    return d == 64 ? SaveLayout<64>{nch, nwc}.floats() : SaveLayout<32>{nch, nwc}.floats();
+}
 
 // Floats of one chain's forward record (the longest over the active routes),
 // 64-float aligned.
-long long record_chain_floats(int H, int W, unsigned mask, const srnl_params *p)
+long long record_chain_floats(int d, int H, int W, unsigned mask, const srnl_params *p)
 {
     const long long N = static_cast<long long>(H) * W;
     long long m = 0;
@@ -2210,7 +2236,7 @@ long long record_chain_floats(int H, int W, unsigned mask, const srnl_params *p)
             L = N;
         if (L < 1)
             L = 1;
-        const long long f = SaveLayout<32>{(N + L - 1) / L, (L + 15) / 16}.floats();
+        const long long f = record_floats(d, (N + L - 1) / L, (L + 15) / 16);
         if (f > m)
             m = f;
     }
@@ -2221,11 +2247,11 @@ long long record_chain_floats(int H, int W, unsigned mask, const srnl_params *p)
 // backward does not apply), 256-byte aligned; -1 past 2^62 bytes.
 long long record_bytes(int B, int H, int W, int heads, int d, unsigned mask, const srnl_params *p)
 {
-    if (!(p->flags & F_RECORD) || !bwd_windowed(d, p))
+    if (!(p->flags & F_RECORD) || !bwd_windowed(d, p, H, W, mask))
         return 0;
     const long long chains = static_cast<long long>(popcount4(mask)) * B * heads;
     long long f = 0;
-    if (__builtin_mul_overflow(chains, record_chain_floats(H, W, mask, p), &f) ||
+    if (__builtin_mul_overflow(chains, record_chain_floats(d, H, W, mask, p), &f) ||
         f > (1LL << 60) - 64)
         return -1;
     return (f * 4 + 255) / 256 * 256;
@@ -2235,7 +2261,7 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
                      const srnl_params *p)
 {
     BwdLayout l;
-    const bool wy = bwd_windowed(d, p);
+    const bool wy = bwd_windowed(d, p, H, W, mask);
     const int R = popcount4(mask);
     const long long N = static_cast<long long>(H) * W;
     const long long rows = 3LL * d + 2;
@@ -2249,7 +2275,7 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
         if (L < 1)
             L = 1;
         const long long nch = (N + L - 1) / L;
-        const long long f = wy ? SaveLayout<32>{nch, (L + 15) / 16}.floats()
+        const long long f = wy ? record_floats(d, nch, (L + 15) / 16)
                                : nch * rows * d + L * d * d + rows * d;
         if (f > l.chain_floats)
             l.chain_floats = f;
@@ -2287,31 +2313,48 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
                            p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
     };
     srnl_status s;
-    if constexpr (D == 32) {
-        if (bwd_windowed(D, p)) {
+    if constexpr (D == 32 || D == 64) {
+        if (bwd_windowed(D, p, H, W, mask)) {
             // the forward record (from the caller's forward, or recorded
             // here), then the windowed backward
             const int nblocks = (nchains + 7) / 8 * 8;
             const FwdSave sv{l.record_given ? static_cast<float *>(p->workspace) : ws,
                              l.chain_floats};
             if (!l.record_given) {
-                s = launch_record_fwd<InT>(x, p, B, H, W, C, heads, mask, nullptr, sv);
+                s = launch_record_fwd<D, InT>(x, p, B, H, W, C, heads, mask, nullptr, sv);
                 if (s != SRNL_OK)
                     return s;
             }
-            auto gw = [&](auto kern) {
-                hipLaunchKernelGGL(kern, dim3(nblocks), dim3(wyb::NT), 0, st,
+            auto gw = [&](auto kern, int nt) {
+                hipLaunchKernelGGL(kern, dim3(nblocks), dim3(nt), 0, st,
                                    static_cast<const InT *>(x), static_cast<const InT *>(p->q), dy,
                                    sv, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
                                    p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
             };
-            if (p->q)
-                gw(scan_bwd_wy_kernel<true, InT>);
-            else
-                gw(scan_bwd_wy_kernel<false, InT>);
-            s = launch_check("scan_bwd_wy_kernel");
+            if constexpr (D == 32) {
+                if (p->q)
+                    gw(scan_bwd_wy_kernel<true, InT>, wyb::NT);
+                else
+                    gw(scan_bwd_wy_kernel<false, InT>, wyb::NT);
+                s = launch_check("scan_bwd_wy_kernel");
+            } else {
+                if (p->q)
+                    gw(scan_bwd_wy64_kernel<true, InT>, wy1::NT);
+                else
+                    gw(scan_bwd_wy64_kernel<false, InT>, wy1::NT);
+                s = launch_check("scan_bwd_wy64_kernel");
+            }
         } else {
-            go(scan_bwd_kernel<D, true, InT>);
+            // the sequential adjoint: reading before the write, or (d = 64)
+            // chunks longer than one window
+            if constexpr (D == 64) {
+                if (p->flags & F_READ_BEFORE)
+                    go(scan_bwd_kernel<D, true, InT>);
+                else
+                    go(scan_bwd_kernel<D, false, InT>);
+            } else {
+                go(scan_bwd_kernel<D, true, InT>);
+            }
             s = launch_check("scan_bwd_kernel");
         }
     } else {
@@ -2583,10 +2626,15 @@ srnl_status srnl_scan_fwd(const void *x, int B, int H, int W, int C, int heads, 
             return s;
     }
     if (rec > 0) {
-        const FwdSave sv{static_cast<float *>(p->workspace), record_chain_floats(H, W, route_mask, p)};
-        s = (p->in_dtype == SRNL_F32)
-                ? launch_record_fwd<float>(x, p, B, H, W, C, heads, route_mask, out, sv)
-                : launch_record_fwd<uint16_t>(x, p, B, H, W, C, heads, route_mask, out, sv);
+        const FwdSave sv{static_cast<float *>(p->workspace), record_chain_floats(d, H, W, route_mask, p)};
+        if (d == 64)
+            s = (p->in_dtype == SRNL_F32)
+                    ? launch_record_fwd<64, float>(x, p, B, H, W, C, heads, route_mask, out, sv)
+                    : launch_record_fwd<64, uint16_t>(x, p, B, H, W, C, heads, route_mask, out, sv);
+        else
+            s = (p->in_dtype == SRNL_F32)
+                    ? launch_record_fwd<32, float>(x, p, B, H, W, C, heads, route_mask, out, sv)
+                    : launch_record_fwd<32, uint16_t>(x, p, B, H, W, C, heads, route_mask, out, sv);
     } else {
         s = (p->in_dtype == SRNL_F32)
                 ? dispatch_scan<float>(d, x, p, B, H, W, C, heads, route_mask, out)

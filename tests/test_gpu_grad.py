@@ -146,6 +146,46 @@ def test_grad_separate_queries_f32_d32():
     run_case(_wl("gq32", 2, 5, 6, 2, 32, dtype="f32", seed=8, separate_q=True))
 
 
+# d = 64 without FLAG_READ_BEFORE, when no route's chunk is longer than 16
+# tokens, takes the single-window windowed backward (one 16-token window per
+# chunk, Q_0 = I); longer chunks and reading before the write take the
+# sequential adjoint.
+def test_grad_d64_plain14_map():
+    """The plain backbone's map: 14x14, C = 192, 3 heads x d = 64, bf16, four
+    routes, 14-token chunks."""
+    run_case(_wl("gp14", 1, 14, 14, 3, 64, dtype="bf16", seed=61, x_kind="ar1"))
+
+
+@pytest.mark.parametrize("flags", [srnl.FLAG_HARD_CAP, srnl.FLAG_NO_CAP, srnl.FLAG_NO_CLAMP,
+                                   srnl.FLAG_FIXED_ALPHA, srnl.FLAG_FREEZE_KV,
+                                   srnl.FLAG_READ_BEFORE])
+def test_grad_variants_d64(flags):
+    std = 0.3 if flags == srnl.FLAG_NO_CAP else 1.0
+    run_case(_wl("gv64", 2, 5, 7, 1, 64, seed=70 + flags, state_std=std), flags=flags)
+
+
+def test_grad_stressed_inputs_d64():
+    run_case(_wl("gadv64", 1, 7, 9, 2, 64, seed=79, state_std=2.0, outlier_frac=0.1))
+
+
+@pytest.mark.parametrize("cr,cc", [(5, 3), (1, 1), (16, 16), (17, 4)])
+def test_grad_chunk_overrides_d64(cr, cc):
+    """Ragged chunks inside one window, one-token chunks, full windows, and a
+    17-token row chunk (the sequential adjoint)."""
+    run_case(_wl("gch64", 1, 6, 19, 1, 64, seed=cr * 7 + cc, state_std=0.5,
+                 chunk_row=cr, chunk_col=cc))
+
+
+@pytest.mark.parametrize("mask", [1, 2, 4, 8, 6, 9])
+def test_grad_route_masks_d64(mask):
+    run_case(_wl("gm64", 2, 4, 6, 1, 64, seed=80 + mask), mask=mask)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grad_separate_queries_d64(dtype):
+    run_case(_wl("gq64", 2, 5, 6, 2, 64, dtype=dtype, seed=90, separate_q=True))
+
+
 def test_grad_is_deterministic():
     wl = _wl("gdet", 2, 5, 5, 2, 16, seed=3)
     a, _ = run_case(wl)
@@ -284,7 +324,7 @@ def test_backward_on_a_side_stream_matches():
 
 
 @pytest.mark.parametrize("case", ["hier", "long_q_f32", "ragged_q_f32", "short_chunks", "t32",
-                                  "variants", "fixed_alpha"])
+                                  "variants", "fixed_alpha", "plain14_d64", "ragged_q_d64"])
 def test_forward_record_matches(case):
     """SRNL_FLAG_RECORD: the forward that keeps its record gives the plain
     forward's outputs bitwise, and the backward that reads that record gives
@@ -305,6 +345,12 @@ def test_forward_record_matches(case):
         wl = _wl("rec_v", 2, 12, 17, 2, 32, dtype="f32", seed=25, state_std=2.0,
                  outlier_frac=0.05)
         flags = srnl.FLAG_HARD_CAP | srnl.FLAG_NO_CLAMP | srnl.FLAG_FREEZE_KV
+    elif case == "plain14_d64":
+        wl = _wl("rec_p", 2, 14, 14, 3, 64, dtype="bf16", seed=31)
+    elif case == "ragged_q_d64":
+        wl = _wl("rec_r", 2, 9, 13, 1, 64, dtype="f32", seed=32, separate_q=True,
+                 chunk_row=5, chunk_col=4)
+        flags = srnl.FLAG_FREEZE_KV
     else:
         wl = _wl("rec_a", 2, 10, 11, 2, 32, dtype="bf16", seed=26)
         flags = srnl.FLAG_FIXED_ALPHA
@@ -329,15 +375,24 @@ def test_forward_record_matches(case):
 
 
 def test_forward_record_where_it_does_not_apply_and_errors():
-    """d = 16 and the readout-before-write variant have no record: the
-    forward runs plainly and the binding returns None. A record smaller than
-    the sizes need is a workspace error in both directions."""
+    """d = 16, d = 64 with chunks longer than 16 tokens and the readout-
+    before-write variant have no record: the forward runs plainly and the
+    binding returns None. A record smaller than the sizes need is a workspace
+    error in both directions."""
     print("[gpu] record n/a and errors", flush=True)
     wl = _wl("rec_n", 2, 5, 6, 2, 16, dtype="f32", seed=27)
     x = torch.from_numpy(wl.x).to(DEV)
     st = torch.from_numpy(wl.states).to(DEV)
     y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15)
     assert rec is None and torch.equal(y, srnl.scan_fwd(x, st, wl.heads, wl.d, 15))
+    # d = 64 with a route's chunks longer than one window: no record either
+    wl = _wl("rec_n64", 1, 4, 17, 1, 64, dtype="f32", seed=30)
+    x = torch.from_numpy(wl.x).to(DEV)
+    st = torch.from_numpy(wl.states).to(DEV)
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15)
+    assert rec is None and torch.equal(y, srnl.scan_fwd(x, st, wl.heads, wl.d, 15))
+    y, rec = srnl.scan_fwd_record(x, st, wl.heads, wl.d, 15, chunk_row=16)
+    assert rec is not None
     wl = _wl("rec_e", 2, 5, 6, 2, 32, dtype="f32", seed=28)
     x = torch.from_numpy(wl.x).to(DEV)
     st = torch.from_numpy(wl.states).to(DEV)
