@@ -564,7 +564,8 @@ def main_bwd(args, wl_name):
     dL/d(fused output), forward outputs and inputs resident in HBM. hier56:
     the hierarchical stage-1 map (d = 32: recording forward + windowed
     adjoint); plain14: the plain backbone's map (B=32, 14x14, C=192, 3 heads
-    of d=64: the sequential adjoint)."""
+    of d=64, chunks of 14 tokens: recording forward + the single-window
+    adjoint at d = 64)."""
     import numpy as np
     import torch
     from self_referential_memory_amd import srnl, synth
@@ -662,21 +663,16 @@ def main_bwd(args, wl_name):
     if wl_name == "hier56":
         what = ("hier56_bwd: backward of the hier56 step (srnl_fuse_bwd + srnl_scan_bwd), "
                 "B=64, 56x56, C=64, 2 heads x d=32, 4 routes")
-        # the d = 32 scan backward (recording forward + windowed adjoint) runs
-        # its contractions on fp32 MFMA
-        roof = {"kernel": "scan_bwd (recording forward + scan_bwd_wy_kernel)", "bound": "mfma",
-                "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_FP32_MFMA_TFLOPS}
+        kern = "scan_bwd (recording forward + scan_bwd_wy_kernel)"
     else:
         what = ("plain14_bwd: backward of the plain14 step (srnl_fuse_bwd + srnl_scan_bwd), "
                 "B=32, 14x14, C=192, 3 heads x d=64, 4 routes")
-        # the d = 64 scan backward is the sequential adjoint on the fp32
-        # vector units; its peak is the fp32 vector figure (157.3 TFLOP/s with
-        # two-wide fp32 instructions, which this build does not emit: half
-        # of it, 78.6, is the ceiling of the scalar fp32 FMAs it issues)
-        roof = {"kernel": "scan_bwd_kernel<64> (sequential adjoint)", "bound": "alu",
-                "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS / 2, "unit": "TFLOP/s",
-                "frac": achieved / (PEAK_FP32_MFMA_TFLOPS / 2)}
+        kern = "scan_bwd (recording forward + scan_bwd_wy64_kernel)"
+    # both scan backwards (recording forward + windowed adjoint) run their
+    # contractions on fp32 MFMA
+    roof = {"kernel": kern, "bound": "mfma", "achieved": achieved,
+            "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA_TFLOPS}
     roof.update({"traffic": None, "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops})
     rec = {
         "metric": "SRNL bwd tokens·heads/s (4 routes) at stage shapes",

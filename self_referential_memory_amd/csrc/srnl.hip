@@ -125,7 +125,29 @@ __device__ __forceinline__ float quad_sum(float v)
     return v;
 }
 
-__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float sigmoidf(float z)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+// tanh(u) for u >= 0, branch-free: below 0.3 the odd Taylor polynomial
+// through u^13 (the first term left out is under 1e-10 of the value there),
+// above it (1 - e) / (1 + e) with e = exp(-2u), where 1 - e >= 0.45 and so
+// loses nothing to cancellation; a few ulp either way.
+__device__ __forceinline__ float tanh_pos(float u)
+{
+    const float u2 = u * u;
+    float p = 21844.0f / 6081075.0f;
+    p = fmaf(p, u2, -1382.0f / 155925.0f);
+    p = fmaf(p, u2, 62.0f / 2835.0f);
+    p = fmaf(p, u2, -17.0f / 315.0f);
+    p = fmaf(p, u2, 2.0f / 15.0f);
+    p = fmaf(p, u2, -1.0f / 3.0f);
+    const float ts = fmaf(u * u2, p, u);
+    const float e = __builtin_amdgcn_exp2f(u * -2.8853900817779268f);   // exp(-2u)
+    const float tl = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+    return u < 0.3f ? ts : tl;
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8 picks
 // the XCD); give each XCD a contiguous range of chains so that chains that
@@ -280,7 +302,7 @@ __global__ __launch_bounds__(ScanCfg<D>::NT) void scan_simple_kernel(
                 } else if (g > 0.0f) {
                     const float uu = eta * g / m;
                     eta1 = (uu < 1e-3f) ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
-                                        : m * tanhf(uu) / g;
+                                        : m * tanh_pos(uu) / g;
                 }
                 float eta2 = eta1;
                 if (!(flags & F_NO_CLAMP) && nkh2 > 0.0f) {
@@ -1121,7 +1143,9 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         const int tm_ph = (GS > 1) ? wave / GT : 0;        // this wave's token tiles tm_ph + GS k
         for (int tn = (GS > 1) ? wave % GT : wave; tn < GT; tn += (GS > 1) ? GT : NW) {
             float *dst = (tn < NTC) ? KZ : Es;
-            const int oc = (tn % NTC) * 16 + lm;
+            // the transposed product [k | v]^T = [B_k; B_v] X^T leaves four
+            // consecutive output channels oc0.. of one token in each lane
+            const int oc0 = (tn % NTC) * 16 + 4 * lk;
             const int brow = D + tn * 16 + lm;   // boundary row of this lane
             if constexpr (std::is_same<InT, uint16_t>::value) {
                 constexpr int KB = D / 32;
@@ -1148,13 +1172,11 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bl[kb], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bm[kb], acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[k][kb], bh[kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[kb], xa[k][kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bm[kb], xa[k][kb], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[kb], xa[k][kb], acc, 0, 0, 0);
                     }
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        dst[ix(tm * 16 + 4 * lk + rr, oc)] = acc[rr];
+                    st4(dst + ix(tm * 16 + lm, oc0), acc[0], acc[1], acc[2], acc[3]);
                 }
             } else {
                 float bg[KS];
@@ -1167,10 +1189,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        acc = mfma4(a[s], bg[s], acc);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        dst[ix(tm * 16 + 4 * lk + rr, oc)] = acc[rr];
+                        acc = mfma4(bg[s], a[s], acc);
+                    st4(dst + ix(tm * 16 + lm, oc0), acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }
@@ -1222,7 +1242,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                 const float eta = sigmoidf(er);
                 const float alpha = (flags & F_FIXED_ALPHA) ? alpha_max
                                                             : alpha_max * sigmoidf(ar);
-                const float g = sqrtf(ne2 * nkh2);
+                const float g = __builtin_amdgcn_sqrtf(ne2 * nkh2);
                 const float m = 1.0f - alpha;
                 float eta1 = eta, uu = 0.f;
                 int bits = 0;
@@ -1237,7 +1257,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     uu = eta * g * __builtin_amdgcn_rcpf(m);
                     const bool series = uu < 1e-3f;
                     eta1 = series ? eta * (1.0f - uu * uu * (1.0f / 3.0f))
-                                  : m * tanhf(uu) * __builtin_amdgcn_rcpf(g);
+                                  : m * tanh_pos(uu) * __builtin_amdgcn_rcpf(g);
                     if (series)
                         bits |= SCB_SERIES;
                 }
@@ -1286,7 +1306,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                                 ke = 1.0f - uu * uu * (1.0f / 3.0f);
                                 kuu = eta * (-2.0f * uu * (1.0f / 3.0f));
                             } else {
-                                const float th = tanhf(uu);
+                                const float th = tanh_pos(uu);
                                 km = th / g;
                                 kuu = m * (1.0f - th * th) / g;
                                 kg = -m * th / (g * g);
@@ -1353,12 +1373,38 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
             const int tb = 16 * win;
             // Gram matrices on MFMA: gkk[i] = k^_s . k^_t, gqk[i] = k^_s . q_t
             v4f gkk = {0.f, 0.f, 0.f, 0.f}, gqk = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (std::is_same<InT, uint16_t>::value && !HAS_Q) {
+                // the query rows are the bf16 input (exact in bf16): k^ split
+                // exactly into three bf16 parts gives k^ . q from three exact
+                // bf16 products per 32 channels; k^ . k^ takes the six part
+                // products down to 2^-16 of the leading one (the three left
+                // out are below 2^-23 of it)
 #pragma unroll
-            for (int jt = 0; jt < NTC; ++jt) {
-                const float4 kv = ld4(KHa + ix(tb + lm, 16 * jt + 4 * lk));
-                const float4 qv = ld4(QR + ix(tb + lm, 16 * jt + 4 * lk));
-                gkk = mfma16(kv, kv, gkk);
-                gqk = mfma16(kv, qv, gqk);
+                for (int kb = 0; kb < D / 32; ++kb) {
+                    float kf[8], xf[8];
+                    ldrow(KHa, tb + lm, 32 * kb + 8 * lk, kf);
+                    ldrow(QR, tb + lm, 32 * kb + 8 * lk, xf);
+                    bf16x8 kh, km, kl;
+                    split3_bf16(kf, kh, km, kl);
+                    const bf16x8 xb = pack_bf16_exact(xf);
+                    gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, xb, gqk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, kh, gkk, 0, 0, 0);
+                    gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, xb, gqk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, kl, gkk, 0, 0, 0);
+                    gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, xb, gqk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, km, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, kh, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, km, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, kh, gkk, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int jt = 0; jt < NTC; ++jt) {
+                    const float4 kv = ld4(KHa + ix(tb + lm, 16 * jt + 4 * lk));
+                    const float4 qv = ld4(QR + ix(tb + lm, 16 * jt + 4 * lk));
+                    gkk = mfma16(kv, kv, gkk);
+                    gqk = mfma16(kv, qv, gqk);
+                }
             }
             const int t = lm;
             const float at = AL[tb + t], et = EH[tb + t];
