@@ -1727,12 +1727,50 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
         //     every token tile.
         if constexpr (OUT) {
             constexpr bool BY_TOKENS = NW > NTC;
-            const int tn0 = BY_TOKENS ? 0 : wave, tns = BY_TOKENS ? 1 : NW;
-            const int tm0 = BY_TOKENS ? wave : 0, tms = BY_TOKENS ? NW : 1;
-            for (int tm = tm0; tm < nwin; tm += tms)
+            if constexpr (BY_TOKENS) {
+                // a token tile's z rows once for all its channel tiles, and
+                // every operand read before the first product
+                for (int tm = wave; tm < nwin; tm += NW) {
+                    float a[KS], a2[KS], br[NTC][KS];
+                    ldrow(KZ, tm * 16 + lm, lk * KS, a);
+                    if (JS == 2)
+                        ldrow(KZ2, tm * 16 + lm, lk * KS, a2);
 #pragma unroll
-                for (int tn = tn0; tn < NTC; tn += tns)
-                    readout_tile(tm, tn);
+                    for (int tn = 0; tn < NTC; ++tn)
+                        ldrow(Bs, tn * 16 + lm, lk * KS, br[tn]);
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        asm volatile("" ::"v"(a[s]));
+                        if (JS == 2)
+                            asm volatile("" ::"v"(a2[s]));
+#pragma unroll
+                        for (int tn = 0; tn < NTC; ++tn)
+                            asm volatile("" ::"v"(br[tn][s]));
+                    }
+                    if (JS == 2) {
+#pragma unroll
+                        for (int s = 0; s < KS; ++s)
+                            a[s] += a2[s];
+                    }
+                    const int u0 = tm * 16 + lm;
+#pragma unroll
+                    for (int tn = 0; tn < NTC; ++tn) {
+                        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < KS; ++s)
+                            acc = mfma4(br[tn][s], a[s], acc);
+                        if (u0 < nt) {
+                            float *orow = out + (out_row0 + s0 + u0) * C + static_cast<size_t>(h) * D + 4 * lk;
+                            *reinterpret_cast<float4 *>(orow + tn * 16) =
+                                make_float4(acc[0], acc[1], acc[2], acc[3]);
+                        }
+                    }
+                }
+            } else {
+                for (int tn = wave; tn < NTC; tn += NW)
+                    for (int tm = 0; tm < nwin; ++tm)
+                        readout_tile(tm, tn);
+            }
         }
         v4f pt_d[RTD_D];
         if constexpr (DIRECT) {
