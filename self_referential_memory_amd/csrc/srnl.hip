@@ -1510,8 +1510,8 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                     acc[i] = (4 * g + i == c) ? 1.0f : 0.0f;
                     xf[i] = 0.0f;
                 }
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
+                auto block = [&](auto bbc) {
+                    constexpr int bb = decltype(bbc)::value;
                     // rows of block bb (final in the lanes with g == bb)
                     float xs[4];
                     xs[0] = acc[0];
@@ -1522,7 +1522,7 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         xf[i] = (g == bb) ? xs[i] : xf[i];
-                    if (bb < 3) {
+                    if constexpr (bb < 3) {
                         float xb[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
@@ -1533,6 +1533,20 @@ __global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
                             for (int j = 0; j < 4; ++j)
                                 acc[i] = fmaf(-lrow[i][4 * bb + j], xb[j], acc[i]);
                     }
+                };
+                block(std::integral_constant<int, 0>());
+                block(std::integral_constant<int, 1>());
+                if (nt - tb > 8) {
+                    block(std::integral_constant<int, 2>());
+                    block(std::integral_constant<int, 3>());
+                } else {
+                    // tokens 8 .. 15 of the window are padding: their rows of L
+                    // are zero, so rows 8 .. 15 of T are those of I, which is
+                    // what the lanes of blocks 2 and 3 hold in acc (the same
+                    // values the two skipped steps would leave there)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xf[i] = (g >= 2) ? acc[i] : xf[i];
                 }
                 if constexpr (SAVE)   // T transposed: [c][4 g + i]
                     st4(svc + sl.o_tab(c0 / L, (s0 - c0) / 16 + win) + SaveLayout<D>::TW_T + c * 16 + 4 * g,
