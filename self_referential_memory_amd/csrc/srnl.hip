@@ -813,7 +813,7 @@ __device__ unsigned long long srnl_phase_buf[kPhaseBlocks * kPhaseSlots];
 
 template <int D, int NW, int T, bool BEFORE, bool HAS_Q, typename InT, bool SAVE = false,
           bool OUT = !SAVE>
-__global__ __launch_bounds__(NW * 64) void scan_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 3 : 1) void scan_mfma_kernel(
     const InT *__restrict__ x, const InT *__restrict__ q,
     const float *__restrict__ states, float *__restrict__ out, int B, int H,
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
