@@ -541,7 +541,10 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int NWIN = T / 16;            // windows per sub-block
     static constexpr int EPL = NT / T;             // epilogue lanes per token
     static constexpr int ECPL = D / EPL;           // channels per epilogue lane
-    static constexpr int TE = T > 32 ? T : 32;     // token columns of the e rows
+    // token columns of the e rows: the sub-block's, at least 32, except that
+    // the 16-token sub-block at d = 32 keeps 16 (which brings its LDS
+    // footprint under a sixth of the CU's: six chains a CU)
+    static constexpr int TE = (D == 32 && T == 16) ? 16 : (T > 32 ? T : 32);
     static constexpr int ETS = TE + 4;             // [channel][token] row stride
     static constexpr int WS = 20;                  // row stride of the per-window L tables
     // row stride of the per-window N tables: as WS, except with separate
@@ -878,7 +881,10 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
     constexpr int EPL = Cfg::EPL, ECPL = Cfg::ECPL, TE = Cfg::TE;
     constexpr int ET_SW = (32 / EPL < 4) ? 4 : 32 / EPL;
     auto et_col = [](int row, int u) {
-        return u ^ ((((row / ECPL) & (EPL - 1)) * ET_SW) & (TE - 4));
+        if constexpr (TE == 16)   // (by groups of 8 channels: no bank shared by the storing lanes)
+            return u ^ (((row / 8) & 3) << 2);
+        else
+            return u ^ ((((row / ECPL) & (EPL - 1)) * ET_SW) & (TE - 4));
     };
 
     const int chain = xcd_remap(blockIdx.x, gridDim.x);
