@@ -1381,10 +1381,10 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
             v4f gkk = {0.f, 0.f, 0.f, 0.f}, gqk = {0.f, 0.f, 0.f, 0.f};
             if constexpr (std::is_same<InT, uint16_t>::value && !HAS_Q) {
                 // the query rows are the bf16 input (exact in bf16): k^ split
-                // exactly into three bf16 parts gives k^ . q from three exact
-                // bf16 products per 32 channels; k^ . k^ takes the six part
-                // products down to 2^-16 of the leading one (the three left
-                // out are below 2^-23 of it)
+                // exactly into three bf16 parts gives k^ . q from three bf16
+                // products per 32 channels and k^ . k^ from all nine part
+                // products; every product is exact and the sums are fp32, as
+                // in the fp32 instruction (smallest parts first)
 #pragma unroll
                 for (int kb = 0; kb < D / 32; ++kb) {
                     float kf[8], xf[8];
@@ -1394,10 +1394,13 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
                     split3_bf16(kf, kh, km, kl);
                     const bf16x8 xb = pack_bf16_exact(xf);
                     gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, xb, gqk, 0, 0, 0);
-                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, kh, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, kl, gkk, 0, 0, 0);
                     gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, xb, gqk, 0, 0, 0);
-                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, kl, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, km, gkk, 0, 0, 0);
                     gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, xb, gqk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, kl, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, kh, gkk, 0, 0, 0);
+                    gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, kl, gkk, 0, 0, 0);
                     gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, km, gkk, 0, 0, 0);
                     gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(km, kh, gkk, 0, 0, 0);
                     gkk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, km, gkk, 0, 0, 0);
