@@ -86,13 +86,14 @@ def test_branch_free_tanh_within_a_few_ulp():
 
 
 def test_sigmoid_as_exp2_and_reciprocal_within_a_few_ulp():
-    """Within 3 ulp, plus |z| ulp from rounding the argument z log2(e) to
-    fp32 (that rounding moves 2^y by |y| 2^-24 ln 2 = |z| 2^-24 relative): at
-    most 2e-6 relative on [-30, 30], where sigmoid(-30) is 1e-13."""
+    """Within 4 ulp, plus up to 2 |z| ulp from the fp32 argument y = z log2(e)
+    (log2(e) rounded to fp32, and the product rounded: each moves 2^y by up to
+    |y| 2^-24 ln 2 = |z| 2^-24 relative): at most 4e-6 relative on [-30, 30],
+    where sigmoid(-30) is 1e-13; within 3 ulp for z >= 0."""
     z = np.linspace(-30.0, 30.0, 200_001).astype(np.float32)
     e = np.exp2((z * f32(-1.4426950408889634)).astype(np.float32)).astype(np.float32)
     got = (f32(1) / (f32(1) + e)).astype(np.float64)
     ref = 1.0 / (1.0 + np.exp(-z.astype(np.float64)))
     ulps = np.abs(got - ref) / (ref * 2.0 ** -24)
-    assert (ulps <= 3.0 + np.abs(z)).all(), (ulps - np.abs(z)).max()
+    assert (ulps <= 4.0 + 2.0 * np.abs(z)).all(), (ulps - 2.0 * np.abs(z)).max()
     assert (ulps[z >= 0] <= 3.0).all()
