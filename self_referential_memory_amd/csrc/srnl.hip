@@ -526,7 +526,7 @@ __device__ __forceinline__ v4f mfma16(const float4 &a, const v4f &b, v4f c)
     return c;
 }
 
-template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
+template <int D, int NW_, int T, bool HAS_Q, bool DEF = false> struct MCfg {
     static constexpr int NW = NW_;                 // waves per chain
     static constexpr int NT = NW * 64;             // threads
     static constexpr int ROWS = 3 * D + 2;
@@ -584,10 +584,12 @@ template <int D, int NW_, int T, bool HAS_Q> struct MCfg {
     static constexpr int WSTR_N = WL ? 16 * LDP : 16 * NS;   // N table stride per window
     static_assert(!WL || (16 * WS <= 16 * LDP && 16 * NS + (TP_IN_ES ? 256 : 0) <= 16 * LDP),
                   "window tables fit the window's rows");
-    static constexpr bool QT_IN_ES = SZ_QT <= SZ_TOK;
+    // (with DEF, the deferred refresh of M_c, Q_L^T keeps an array of its
+    // own: it is read again in the next sub-block's table phase)
+    static constexpr bool QT_IN_ES = !DEF && SZ_QT <= SZ_TOK;
     // else, when it fits, over the x, k/z, v and k^ rows (contiguous), which
     // are dead at a chunk end once the readout has read the z rows
-    static constexpr bool QT_IN_TOK = !QT_IN_ES && SZ_QT <= 4 * SZ_TOK;
+    static constexpr bool QT_IN_TOK = !DEF && !QT_IN_ES && SZ_QT <= 4 * SZ_TOK;
     static constexpr int O_BS = 0;
     static constexpr int O_XS = O_BS + ROWS * LDP;
     static constexpr int O_KZ = O_XS + SZ_TOK;
@@ -822,7 +824,13 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
     int W, int C, int heads, unsigned route_mask, int R, float alpha_max,
     float eps, int chunk_row, int chunk_col, unsigned flags, int nchains, FwdSave sv)
 {
-    using Cfg = MCfg<D, NW, T, HAS_Q>;
+    // The refresh of M_c (the readout memory) is deferred to the next
+    // sub-block's table phase in the long sub-blocks at d = 32: the next
+    // chunk's generation and epilogue read only M_k, M_v and the vector
+    // memories, and its readout, the first reader of M_c, comes after its
+    // update. The chunk end then refreshes 8 of the 12 tiles.
+    static constexpr bool DEFER_MC = D == 32 && T >= 64 && !SAVE && OUT && !HAS_Q;
+    using Cfg = MCfg<D, NW, T, HAS_Q, DEFER_MC>;
     constexpr int NT = Cfg::NT, ROWS = Cfg::ROWS, LDP = Cfg::LDP, KS = Cfg::KS,
                   NTC = Cfg::NTC, ETS = Cfg::ETS, WS = Cfg::WS, NS = Cfg::NS, JS = Cfg::JS, NJ = Cfg::NJ,
                   CW = Cfg::CW, NWIN = Cfg::NWIN;
@@ -975,6 +983,7 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
     const unsigned long long ph_t0 = ph_t;
 #endif
     const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
+    bool mc_pending = false;   // M_c still waits for the last chunk's Q_L (DEFER_MC)
     // The direct refresh of a single-window chunk (DIRECT):
     //   B' = G_15 B + P diag(R[15]) K^,  P = B U^T  [row][token],
     // with U staged over the query rows by the update. P is formed per
@@ -1373,6 +1382,21 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
             __syncthreads();
         SRNL_PHASE(2);
 
+        // deferred M_c refresh, products: wave w < NTC^2 takes tile (w / NTC,
+        // w % NTC) of M_c Q_L into registers; stored after this phase's
+        // closing barrier (every wave has read M_c by then)
+        v4f mc_acc = {0.f, 0.f, 0.f, 0.f};
+        const bool do_mc = DEFER_MC && mc_pending && wave < NTC * NTC;
+        if constexpr (DEFER_MC) {
+            if (do_mc) {
+                float a[KS], bq[KS];
+                ldrow(Bs, (wave / NTC) * 16 + lm, lk * KS, a);
+                ldrow(Qt, (wave % NTC) * 16 + lm, lk * KS, bq);
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    mc_acc = mfma4(bq[s], a[s], mc_acc);
+            }
+        }
         // (4) window tables, wave w for windows w, w + NW, ... (window-local
         //     token indices t, s in 0..15; lane holds s = 4 lk + i, t = lm)
         for (int win = wave; win < nwin; win += NW) {
@@ -1568,6 +1592,12 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
             }
         }
         __syncthreads();
+        if constexpr (DEFER_MC) {
+            if (do_mc)   // transposed product: four consecutive channels of one row
+                st4(Bs + ix((wave / NTC) * 16 + lm, (wave % NTC) * 16 + 4 * lk), mc_acc[0], mc_acc[1],
+                    mc_acc[2], mc_acc[3]);
+            mc_pending = false;
+        }
         SRNL_PHASE(3);
 
         // (5) token-order update, window by window, on MFMA. Wave w owns rows
@@ -1819,11 +1849,14 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
                             stage_qt();
                         __syncthreads();
                     }
-                    v4f racc[RTW];
+                    // (with DEFER_MC the M_c tiles wait for the next sub-block)
+                    constexpr int T0 = DEFER_MC ? NTC * NTC : 0;   // first tile refreshed here
+                    constexpr int RTH = RT - T0, RTWH = (RTH + NW - 1) / NW;
+                    v4f racc[RTWH];
 #pragma unroll
-                    for (int w = 0; w < RTW; ++w) {
-                        const int tile = wave + w * NW;
-                        if (RT % NW != 0 && tile >= RT)
+                    for (int w = 0; w < RTWH; ++w) {
+                        const int tile = T0 + wave + w * NW;
+                        if (RTH % NW != 0 && tile >= RT)
                             break;
                         const int tm = tile / NTC, tn = tile % NTC;
                         float a[KS], bq[KS];
@@ -1857,9 +1890,9 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
                     }
                     __syncthreads();
 #pragma unroll
-                    for (int w = 0; w < RTW; ++w) {
-                        const int tile = wave + w * NW;
-                        if (RT % NW != 0 && tile >= RT)
+                    for (int w = 0; w < RTWH; ++w) {
+                        const int tile = T0 + wave + w * NW;
+                        if (RTH % NW != 0 && tile >= RT)
                             break;
                         const int tm = tile / NTC, tn = tile % NTC;
 #pragma unroll
@@ -1869,6 +1902,8 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
                     }
                     if (tid < 2 * D * VG && vpart == 0 && !frz)
                         Bs[ix(3 * D + vv, vj)] = vacc;
+                    if constexpr (DEFER_MC)
+                        mc_pending = true;
                 }
             }
             reset_q();
