@@ -953,7 +953,7 @@ def main():
             e["pmc_hbm_bytes"] = prof[name]["hbm_bytes_per_launch"]
             if "mfma" in prof[name]:
                 e["mfma_pipe_util"] = prof[name]["mfma"]["pipe_util"]
-                e["mfma_bf16_TFLOPs_generation"] = prof[name]["mfma"]["bf16_TFLOPs"]
+                e["mfma_bf16_TFLOPs_generation_and_grams"] = prof[name]["mfma"]["bf16_TFLOPs"]
             if "valu" in prof[name]:
                 e["valu_busy"] = prof[name]["valu"]["busy"]
                 e["wait_inst_frac"] = prof[name]["valu"]["wait_inst_frac"]
