@@ -806,11 +806,15 @@ constexpr int SCB_SERIES = 1, SCB_HARD = 2, SCB_CLAMP = 4;
 #if SRNL_PHASE_CLOCKS
 constexpr int kPhaseBlocks = 16384, kPhaseSlots = 15;
 __device__ unsigned long long srnl_phase_buf[kPhaseBlocks * kPhaseSlots];
+// (the per-phase sums live in LDS, ph_lds, added to by lane 0 of wave 0
+// without waiting for a return, so the stamps cost the instrumented kernel
+// no registers beyond the last clock reading)
 #define SRNL_PHASE(k)                                                                \
     do {                                                                             \
         if (wave == 0) {                                                             \
             const unsigned long long t_ = clock64();                                 \
-            ph_acc[k] += t_ - ph_t;                                                  \
+            if (lane == 0)                                                           \
+                atomicAdd(&ph_lds[k], static_cast<unsigned>(t_ - ph_t));             \
             ph_t = t_;                                                               \
         }                                                                            \
     } while (0)
@@ -981,7 +985,10 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
 
     float *const svc = SAVE ? sv.base + static_cast<long long>(chain) * sv.chain_floats : nullptr;
 #if SRNL_PHASE_CLOCKS
-    unsigned long long ph_acc[7] = {0, 0, 0, 0, 0, 0, 0}, ph_n = 0, ph_t = clock64();
+    __shared__ unsigned ph_lds[16];
+    if (tid < 16)
+        ph_lds[tid] = 0u;
+    unsigned long long ph_n = 0, ph_t = clock64();
     const unsigned long long ph_t0 = ph_t;
 #endif
     const SaveLayout<D> sl{(N + L - 1) / L, (L + 15) / 16};
@@ -1925,7 +1932,7 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
     if (wave == 0 && lane == 0 && blockIdx.x < kPhaseBlocks) {
         unsigned long long *o = srnl_phase_buf + blockIdx.x * kPhaseSlots;
         for (int k = 0; k < kPhaseSlots - 2; ++k)
-            o[k] = (k < 7) ? ph_acc[k] : 0;
+            o[k] = (k < 7) ? ph_lds[k] : 0;
         o[kPhaseSlots - 2] = ph_n;
         o[kPhaseSlots - 1] = clock64() - ph_t0;
     }
