@@ -2518,12 +2518,13 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
     if (s != SRNL_OK)
         return s;
     const long long n = static_cast<long long>(B) * H * W * C;
-    hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dxr, dx, R, n);
+    hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, dxr, dx, R, n);
     if (p->q)
-        hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dqr, dq, R, n);
+        hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, dqr, dq, R, n);
     const int sz = 3 * D * D + 2 * D;
-    hipLaunchKernelGGL(states_grad_kernel, dim3(grid_for(static_cast<long long>(nr_out) * heads * sz, 256)),
-                       dim3(256), 0, st, dstp, dstates, B, heads, R, mask, sz, nr_out);
+    const long long nst = static_cast<long long>(nr_out) * heads * sz;
+    hipLaunchKernelGGL(states_grad_kernel, dim3(static_cast<unsigned>((nst + 63) / 64)), dim3(256), 0, st,
+                       dstp, dstates, B, heads, R, mask, sz, nr_out);
     return launch_check("scan_bwd reductions");
 }
 
