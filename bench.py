@@ -560,8 +560,9 @@ def main_block56(args):
 
 
 def main_bwd(args, wl_name):
-    """Backward of a forward step: srnl_fuse_bwd + srnl_scan_bwd for a given
-    dL/d(fused output), forward outputs and inputs resident in HBM. hier56:
+    """Backward of a forward step: srnl_scan_fuse_bwd (the results of
+    srnl_fuse_bwd + srnl_scan_bwd in one call) for a given dL/d(fused output),
+    forward outputs and inputs resident in HBM. hier56:
     the hierarchical stage-1 map (d = 32: recording forward + windowed
     adjoint); plain14: the plain backbone's map (B=32, 14x14, C=192, 3 heads
     of d=64, chunks of 14 tokens: recording forward + the single-window
@@ -582,29 +583,25 @@ def main_bwd(args, wl_name):
     p = srnl.make_params(st, x)
     L = srnl.lib()
     import ctypes
-    nb_s = L.srnl_scan_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
-                                           ctypes.byref(p))
-    nb_f = L.srnl_fuse_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, 15)
+    nb_s = L.srnl_scan_fuse_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                                ctypes.byref(p))
     ws_s = torch.empty(nb_s, dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(nb_f, dtype=torch.uint8, device=dev)
-    dyr = torch.empty_like(y)
     dsc = torch.empty((4, wl.C), dtype=torch.float32, device=dev)
     dx = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.float32, device=dev)
     dst = torch.empty_like(st)
     stream = torch.cuda.current_stream().cuda_stream
 
     def step(a=None, b=None):
-        L.srnl_fuse_bwd(dout.data_ptr(), y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15,
-                        sc.data_ptr(), dyr.data_ptr(), dsc.data_ptr(), ws_f.data_ptr(), nb_f, stream)
         if a is not None:
             a.record()
-        rc = L.srnl_scan_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
-                             ctypes.byref(p), dyr.data_ptr(), ws_s.data_ptr(), nb_s,
-                             dx.data_ptr(), None, dst.data_ptr())
+        rc = L.srnl_scan_fuse_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                  ctypes.byref(p), y.data_ptr(), sc.data_ptr(), dout.data_ptr(),
+                                  ws_s.data_ptr(), nb_s, dx.data_ptr(), None, dst.data_ptr(),
+                                  dsc.data_ptr())
         if b is not None:
             b.record()
         if rc != 0:
-            raise RuntimeError(f"srnl_scan_bwd failed: {rc}")
+            raise RuntimeError(f"srnl_scan_fuse_bwd failed: {rc}")
 
     for _ in range(args.warmup):
         step()
@@ -627,8 +624,8 @@ def main_bwd(args, wl_name):
                                        ctypes.byref(pr))
     ws_r = torch.empty(nb_r, dtype=torch.uint8, device=dev)
     pr.workspace, pr.workspace_bytes = ws_r.data_ptr(), nb_r
-    nb_sr = L.srnl_scan_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
-                                            ctypes.byref(pr))
+    nb_sr = L.srnl_scan_fuse_bwd_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                                 ctypes.byref(pr))
     ws_sr = torch.empty(nb_sr, dtype=torch.uint8, device=dev)
     fused = torch.empty((wl.B, wl.H, wl.W, wl.C), dtype=torch.bfloat16, device=dev)
 
@@ -638,12 +635,10 @@ def main_bwd(args, wl_name):
                              ctypes.byref(pp), y.data_ptr())
         rc |= L.srnl_fuse(y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15, sc.data_ptr(),
                           srnl.SRNL_BF16, fused.data_ptr(), stream)
-        rc |= L.srnl_fuse_bwd(dout.data_ptr(), y.data_ptr(), wl.B, wl.H, wl.W, wl.C, 15,
-                              sc.data_ptr(), dyr.data_ptr(), dsc.data_ptr(), ws_f.data_ptr(),
-                              nb_f, stream)
-        rc |= L.srnl_scan_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
-                              ctypes.byref(pp), dyr.data_ptr(), ws.data_ptr(), nb,
-                              dx.data_ptr(), None, dst.data_ptr())
+        rc |= L.srnl_scan_fuse_bwd(x.data_ptr(), wl.B, wl.H, wl.W, wl.C, wl.heads, wl.d, 15,
+                                   ctypes.byref(pp), y.data_ptr(), sc.data_ptr(), dout.data_ptr(),
+                                   ws.data_ptr(), nb, dx.data_ptr(), None, dst.data_ptr(),
+                                   dsc.data_ptr())
         if rc != 0:
             raise RuntimeError("training step failed")
 
@@ -661,19 +656,24 @@ def main_bwd(args, wl_name):
     flops = 2 * algorithmic_flops_per_unit(wl.d) * units * R
     achieved = flops / (scan_ms / 1000.0) / 1e12
     if wl_name == "hier56":
-        what = ("hier56_bwd: backward of the hier56 step (srnl_fuse_bwd + srnl_scan_bwd), "
+        what = ("hier56_bwd: backward of the hier56 step (srnl_scan_fuse_bwd), "
                 "B=64, 56x56, C=64, 2 heads x d=32, 4 routes")
-        kern = "scan_bwd (recording forward + scan_bwd_wy_kernel)"
+        kern = ("scan_fuse_bwd (fusion backward partial sums + recording forward + "
+                "scan_bwd_wy_kernel reading dout)")
     else:
-        what = ("plain14_bwd: backward of the plain14 step (srnl_fuse_bwd + srnl_scan_bwd), "
+        what = ("plain14_bwd: backward of the plain14 step (srnl_scan_fuse_bwd), "
                 "B=32, 14x14, C=192, 3 heads x d=64, 4 routes")
-        kern = "scan_bwd (recording forward + scan_bwd_wy64_kernel)"
+        kern = ("scan_fuse_bwd (fusion backward + recording forward + "
+                "scan_bwd_wy64_kernel)")
     # both scan backwards (recording forward + windowed adjoint) run their
     # contractions on fp32 MFMA
     roof = {"kernel": kern, "bound": "mfma", "achieved": achieved,
             "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS}
-    roof.update({"traffic": None, "scan_ms": scan_ms, "algorithmic_flops_per_launch": flops})
+    roof.update({"traffic": None, "call_ms": scan_ms,
+                 "timed": "one srnl_scan_fuse_bwd call by HIP events (fusion backward, "
+                          "recording forward, adjoint, reductions)",
+                 "algorithmic_flops_per_launch": flops})
     rec = {
         "metric": "SRNL bwd tokens·heads/s (4 routes) at stage shapes",
         "value": units / (ms / 1000.0), "unit": "tokens·heads/s", "n_gpus": 1,
@@ -685,8 +685,8 @@ def main_bwd(args, wl_name):
                    "routes": R, "input_dtype": "bf16", "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": None,
-        "train_step": {"what": "srnl_scan_fwd + srnl_fuse (bf16 out) + srnl_fuse_bwd + "
-                               "srnl_scan_bwd per step",
+        "train_step": {"what": "srnl_scan_fwd + srnl_fuse (bf16 out) + srnl_scan_fuse_bwd "
+                               "per step",
                        "ms_forward_keeps_record": train_ms[True],
                        "ms_backward_records_again": train_ms[False],
                        "record_bytes": nb_r},

@@ -295,6 +295,38 @@ srnl_status srnl_fuse_bwd(const float *dout, const float *y_routes, int B, int H
                           size_t workspace_bytes, void *stream);
 
 /*
+ * srnl_scan_fuse_bwd_workspace_bytes / srnl_scan_fuse_bwd -- backward of the
+ * whole operator, srnl_fuse after srnl_scan_fwd [README SRNL and VisionHOPE
+ * operator: training with autograd; OVERVIEW Four-Directional Scanning and
+ * Spatial Chunking: the routes' outputs fused with learned per-channel
+ * scales], in one call: the results of srnl_fuse_bwd followed by
+ * srnl_scan_bwd on its dy_routes, without dy_routes in memory where the
+ * windowed d = 32 adjoint runs (d = 32, readout after the write): that
+ * adjoint reads dout at the cells each route visits and multiplies by the
+ * route's scales as it reads them (the same fp32 products, so dx, dq and
+ * dstates are bitwise those of the two calls). Elsewhere dy_routes are
+ * written to the workspace and the two calls' kernels run in turn.
+ *   x, params   as srnl_scan_bwd (the forward's);
+ *   y_routes    [R][B][H*W][C] fp32, the forward's route outputs;
+ *   scales      [4][C] fp32, the fusion's scales;
+ *   dout        [B][H][W][C] fp32 = dL/d(fused output);
+ *   dx, dq, dstates  as srnl_scan_bwd (overwritten);
+ *   dscales     [4][C] fp32 as srnl_fuse_bwd (overwritten).
+ * All on params->stream. The workspace is caller-owned device memory of at
+ * least srnl_scan_fuse_bwd_workspace_bytes(...) bytes (0 for an empty grid
+ * or invalid arguments), 16-byte aligned; its contents are scratch. Sums run
+ * in a fixed order (bitwise reproducible). Errors: as srnl_scan_bwd and
+ * srnl_fuse_bwd (C <= 1024).
+ */
+size_t srnl_scan_fuse_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                          unsigned route_mask, const srnl_params *params);
+srnl_status srnl_scan_fuse_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                               unsigned route_mask, const srnl_params *params,
+                               const float *y_routes, const float *scales, const float *dout,
+                               void *workspace, size_t workspace_bytes, float *dx, float *dq,
+                               float *dstates, float *dscales);
+
+/*
  * srnl_fuse_bwd_noalloc -- srnl_fuse_bwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving or training
  * loops, harnesses that forbid hipMalloc). It takes no workspace: the

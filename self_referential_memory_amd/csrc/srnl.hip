@@ -2451,7 +2451,8 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
 template <int D, typename InT>
 srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
                             int heads, unsigned mask, const float *dy, float *ws,
-                            const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out)
+                            const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out,
+                            const float *ysc)
 {
     const int R = popcount4(mask);
     const int nchains = static_cast<int>(l.chains);
@@ -2483,10 +2484,17 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
                                    p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
             };
             if constexpr (D == 32) {
+                // ysc: dy is the fused output's gradient, scaled per route here
+                auto g32 = [&](auto kern) {
+                    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(wyb::NT), 0, st,
+                                       static_cast<const InT *>(x), static_cast<const InT *>(p->q), dy,
+                                       ysc, sv, B, H, W, C, heads, mask, R, p->alpha_max, p->eps,
+                                       p->chunk_row, p->chunk_col, p->flags, nchains, dxr, dqr, dstp);
+                };
                 if (p->q)
-                    gw(scan_bwd_wy_kernel<true, InT>, wyb::NT);
+                    ysc ? g32(scan_bwd_wy_kernel<true, InT, true>) : g32(scan_bwd_wy_kernel<true, InT>);
                 else
-                    gw(scan_bwd_wy_kernel<false, InT>, wyb::NT);
+                    ysc ? g32(scan_bwd_wy_kernel<false, InT, true>) : g32(scan_bwd_wy_kernel<false, InT>);
                 s = launch_check("scan_bwd_wy_kernel");
             } else {
                 if (p->q)
@@ -2531,14 +2539,15 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
 template <typename InT>
 srnl_status dispatch_scan_bwd(int d, const void *x, const srnl_params *p, int B, int H, int W,
                               int C, int heads, unsigned mask, const float *dy, float *ws,
-                              const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out)
+                              const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out,
+                              const float *ysc)
 {
     switch (d) {
-    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
-    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
-    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
-    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
-    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out);
+    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
+    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
+    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
+    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
+    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
     }
     return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
 }
@@ -2875,11 +2884,13 @@ size_t srnl_scan_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int 
 
 namespace {
 // srnl_scan_bwd, with the state gradients written for route slots
-// 0 .. nr_out - 1 (4 for the 2-D operator, 1 for the 1-D one)
+// 0 .. nr_out - 1 (4 for the 2-D operator, 1 for the 1-D one). With ysc
+// (the windowed d = 32 adjoint only), dy is the fused output's gradient
+// [B][H][W][C] and each route's dy is formed from it with the scales ysc.
 srnl_status scan_bwd_impl(const void *x, int B, int H, int W, int C, int heads, int d,
                           unsigned route_mask, const srnl_params *p, const float *dy,
                           void *workspace, size_t workspace_bytes, float *dx, float *dq,
-                          float *dstates, int nr_out)
+                          float *dstates, int nr_out, const float *ysc = nullptr)
 {
     long long n = 0;
     srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
@@ -2914,9 +2925,9 @@ srnl_status scan_bwd_impl(const void *x, int B, int H, int W, int C, int heads, 
     float *ws = static_cast<float *>(workspace);
     if (p->in_dtype == SRNL_F32)
         return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
-                                        dstates, nr_out);
+                                        dstates, nr_out, ysc);
     return dispatch_scan_bwd<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
-                                       dstates, nr_out);
+                                       dstates, nr_out, ysc);
 }
 
 }   // namespace
@@ -2975,9 +2986,12 @@ size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_
 namespace {
 // srnl_fuse_bwd with its partial sums in `workspace`, or (noalloc) in the
 // library's scratch array of this GPU
+// (dyr NULL with dyr_optional: only dscales; the route gradients are formed
+// by the windowed adjoint itself)
 srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W, int C,
                           unsigned route_mask, const float *scales, float *dyr, float *dscales,
-                          void *workspace, size_t workspace_bytes, void *stream, bool noalloc)
+                          void *workspace, size_t workspace_bytes, void *stream, bool noalloc,
+                          bool dyr_optional = false)
 {
     long long n = 0;
     srnl_status s = check_grid(B, H, W, C, route_mask, &n);
@@ -3001,10 +3015,12 @@ srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W
     }
     if (nblk > 65535LL * 16)
         return fail(SRNL_ERR_ARG, "grid too large for srnl_fuse_bwd");
+    const bool skip_dyr = dyr_optional && dyr == nullptr;
     if (!is_device_ptr(dout) || !is_device_ptr(y) || !is_device_ptr(scales) ||
-        !is_device_ptr(dyr) || !is_device_ptr(dscales) || (!noalloc && !is_device_ptr(workspace)))
+        (!skip_dyr && !is_device_ptr(dyr)) || !is_device_ptr(dscales) ||
+        (!noalloc && !is_device_ptr(workspace)))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be device memory");
-    if (!aligned16(dout) || !aligned16(y) || !aligned16(scales) || !aligned16(dyr) ||
+    if (!aligned16(dout) || !aligned16(y) || !aligned16(scales) || (!skip_dyr && !aligned16(dyr)) ||
         !aligned16(dscales) || (!noalloc && !aligned16(workspace)))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -3043,6 +3059,80 @@ srnl_status srnl_fuse_bwd_noalloc(const float *dout, const float *y, int B, int 
     g_last_error.clear();
     return fuse_bwd_impl(dout, y, B, H, W, C, route_mask, scales, dyr, dscales, nullptr, 0,
                          stream, true);
+}
+
+}   // extern "C"
+
+namespace {
+// Workspace of srnl_scan_fuse_bwd in floats: the scan backward's, the fusion
+// backward's partial sums, and (where the adjoint cannot form each route's
+// dy itself) the route gradients; -1 if too large or invalid.
+struct OpBwdLayout {
+    bool direct = false;     // windowed d = 32 adjoint reads dout and the scales
+    long long scan = 0, part = 0, dyr = 0, total = -1;
+};
+
+long long round64(long long v) { return (v + 63) / 64 * 64; }
+
+OpBwdLayout op_bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask,
+                          const srnl_params *p)
+{
+    OpBwdLayout o;
+    const BwdLayout l = bwd_layout(B, H, W, C, heads, d, mask, p);
+    if (l.total < 0)
+        return o;
+    o.direct = d == 32 && bwd_windowed(d, p, H, W, mask);
+    o.scan = round64(l.total);
+    o.part = round64(static_cast<long long>(popcount4(mask)) * fuse_bwd_blocks(B, H, W) * C);
+    o.dyr = o.direct ? 0 : round64(static_cast<long long>(popcount4(mask)) * B * H * W * C);
+    o.total = o.scan + o.part + o.dyr;
+    return o;
+}
+}   // namespace
+
+extern "C" {
+
+size_t srnl_scan_fuse_bwd_workspace_bytes(int B, int H, int W, int C, int heads, int d,
+                                          unsigned route_mask, const srnl_params *p)
+{
+    long long n = 0;
+    if (check_scan_args(B, H, W, C, heads, d, route_mask, p, &n) != SRNL_OK || n == 0 || C > 1024)
+        return 0;
+    const OpBwdLayout o = op_bwd_layout(B, H, W, C, heads, d, route_mask, p);
+    return o.total < 0 ? 0 : static_cast<size_t>(o.total) * sizeof(float);
+}
+
+srnl_status srnl_scan_fuse_bwd(const void *x, int B, int H, int W, int C, int heads, int d,
+                               unsigned route_mask, const srnl_params *p, const float *y_routes,
+                               const float *scales, const float *dout, void *workspace,
+                               size_t workspace_bytes, float *dx, float *dq, float *dstates,
+                               float *dscales)
+{
+    g_last_error.clear();
+    long long n = 0;
+    srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
+    if (s != SRNL_OK)
+        return s;
+    if (n == 0)
+        return SRNL_OK;   // empty grid
+    if (C > 1024)
+        return fail(SRNL_ERR_ARG, "srnl_scan_fuse_bwd supports C <= 1024");
+    const OpBwdLayout o = op_bwd_layout(B, H, W, C, heads, d, route_mask, p);
+    if (o.total < 0)
+        return fail(SRNL_ERR_ARG, "grid too large for srnl_scan_fuse_bwd's workspace");
+    if (!workspace || workspace_bytes < static_cast<size_t>(o.total) * sizeof(float))
+        return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_scan_fuse_bwd_workspace_bytes");
+    float *ws = static_cast<float *>(workspace);
+    float *part = ws + o.scan, *dyr = o.direct ? nullptr : part + o.part;
+    s = fuse_bwd_impl(dout, y_routes, B, H, W, C, route_mask, scales, dyr, dscales, part,
+                      static_cast<size_t>(o.part) * sizeof(float), p->stream, false, true);
+    if (s != SRNL_OK)
+        return s;
+    if (o.direct)
+        return scan_bwd_impl(x, B, H, W, C, heads, d, route_mask, p, dout, ws,
+                             static_cast<size_t>(o.scan) * sizeof(float), dx, dq, dstates, 4, scales);
+    return scan_bwd_impl(x, B, H, W, C, heads, d, route_mask, p, dyr, ws,
+                         static_cast<size_t>(o.scan) * sizeof(float), dx, dq, dstates, 4);
 }
 
 size_t srnl_block_workspace_bytes(int B, int H, int W, int C, unsigned route_mask)

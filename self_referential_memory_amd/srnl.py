@@ -30,6 +30,7 @@ EXPORTS = ("srnl_scan_fwd", "srnl_scan_workspace_bytes", "srnl_scan_1d",
            "srnl_scan_1d_workspace_bytes", "srnl_fuse", "srnl_scan_bwd",
            "srnl_scan_bwd_workspace_bytes", "srnl_scan_1d_bwd", "srnl_scan_1d_bwd_workspace_bytes",
            "srnl_fuse_bwd", "srnl_fuse_bwd_workspace_bytes", "srnl_fuse_bwd_noalloc",
+           "srnl_scan_fuse_bwd", "srnl_scan_fuse_bwd_workspace_bytes",
            "srnl_route_gather", "srnl_init_states", "srnl_block_fwd",
            "srnl_block_workspace_bytes",
            "srnl_route_index", "srnl_chunk_len", "srnl_status_string",
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.srnl_fuse_bwd_workspace_bytes.restype = sz
         L.srnl_fuse_bwd.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp, sz, vp]
         L.srnl_fuse_bwd_noalloc.argtypes = [vp, vp, i, i, i, i, u, vp, vp, vp, vp]
+        L.srnl_scan_fuse_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, u, ctypes.POINTER(Params)]
+        L.srnl_scan_fuse_bwd_workspace_bytes.restype = sz
+        L.srnl_scan_fuse_bwd.argtypes = [vp, i, i, i, i, i, i, u, ctypes.POINTER(Params), vp, vp,
+                                         vp, vp, sz, vp, vp, vp, vp]
         L.srnl_route_gather.argtypes = [vp, i, i, i, i, u, i, vp, vp]
         L.srnl_init_states.argtypes = [vp, i, i, ctypes.c_ulonglong, ctypes.c_float, vp]
         L.srnl_block_workspace_bytes.argtypes = [i, i, i, i, u]
@@ -103,7 +108,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.POINTER(BlockWeights), vp, sz, vp]
         for f in ("srnl_scan_fwd", "srnl_scan_1d", "srnl_fuse", "srnl_scan_bwd",
                   "srnl_scan_1d_bwd", "srnl_fuse_bwd", "srnl_fuse_bwd_noalloc",
-                  "srnl_route_gather", "srnl_init_states", "srnl_block_fwd"):
+                  "srnl_scan_fuse_bwd", "srnl_route_gather", "srnl_init_states", "srnl_block_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.srnl_route_index.argtypes = [i, i, i, ctypes.c_long, ctypes.POINTER(i),
                                        ctypes.POINTER(i)]
@@ -395,6 +400,40 @@ def fuse_bwd(dout: torch.Tensor, y: torch.Tensor, B: int, H: int, W: int, C: int
     return dyr, dsc
 
 
+def scan_fuse_bwd(x: torch.Tensor, states: torch.Tensor, heads: int, d: int, y: torch.Tensor,
+                  scales: torch.Tensor, dout: torch.Tensor, route_mask: int = 15,
+                  q: Optional[torch.Tensor] = None, *, params: Optional[Params] = None,
+                  record: Optional[torch.Tensor] = None, **kw):
+    """srnl_scan_fuse_bwd: the operator's backward in one call, dout [B,H,W,C]
+    fp32 -> (dx [B,H,W,C], dq or None, dstates [4,heads,3d^2+2d], dscales
+    [4,C]), all fp32; the same results as fuse_bwd then scan_bwd. y: the
+    forward's route outputs [R,B,H*W,C]; ``record`` as for scan_bwd."""
+    B, H, W, C = x.shape
+    R = bin(route_mask & 15).count("1")
+    _expect(states, _state_shape(heads, d), torch.float32, "states")
+    _expect(y, (R, B, H * W, C), torch.float32, "y")
+    _expect(scales, (4, C), torch.float32, "scales")
+    _expect(dout, (B, H, W, C), torch.float32, "dout")
+    p = params if params is not None else make_params(states, x, q, **kw)
+    if record is not None:
+        p = Params.from_buffer_copy(p)
+        p.flags = (p.flags | FLAG_RECORD) & ~FLAG_CHECK_FINITE
+        p.workspace, p.workspace_bytes = record.data_ptr(), record.numel() * record.element_size()
+    nbytes = lib().srnl_scan_fuse_bwd_workspace_bytes(B, H, W, C, heads, d, route_mask,
+                                                      ctypes.byref(p))
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x.device)
+    dx = torch.empty((B, H, W, C), dtype=torch.float32, device=x.device)
+    dq = None if q is None else torch.empty_like(dx)
+    dst = torch.empty((4, heads, 3 * d * d + 2 * d), dtype=torch.float32, device=x.device)
+    dsc = torch.empty((4, C), dtype=torch.float32, device=x.device)
+    _check(lib().srnl_scan_fuse_bwd(_ptr(x), B, H, W, C, heads, d, route_mask, ctypes.byref(p),
+                                    _ptr(y), _ptr(scales), _ptr(dout), _ptr(ws), int(nbytes),
+                                    _ptr(dx), _ptr(dq), _ptr(dst), _ptr(dsc)),
+           "srnl_scan_fuse_bwd")
+    _keep_for_stream(p.stream, ws)
+    return dx, dq, dst, dsc
+
+
 def route_gather(x: torch.Tensor, route_mask: int = 15, out: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
     """srnl_route_gather: x [B,H,W,C] -> [R,B,H*W,C] in route order."""
@@ -439,8 +478,8 @@ def _side_stream(kw):
 
 class Operator(torch.autograd.Function):
     """The operator (scan + fuse) as an autograd node: the forward pass is
-    srnl_scan_fwd and srnl_fuse, the backward pass srnl_fuse_bwd and
-    srnl_scan_bwd. Gradients flow to x, the initial states, the scales and
+    srnl_scan_fwd and srnl_fuse, the backward pass srnl_scan_fuse_bwd (the
+    results of srnl_fuse_bwd then srnl_scan_bwd). Gradients flow to x, the initial states, the scales and
     the separate queries. The route outputs are kept for the fusion backward,
     and, where the windowed backward applies, the forward's record
     (SRNL_FLAG_RECORD), so the backward does not run the forward again.
@@ -483,8 +522,8 @@ class Operator(torch.autograd.Function):
             dout.record_stream(side)
         with torch.cuda.stream(side if side is not None else cur):
             d32 = dout.to(torch.float32).contiguous()
-            dyr, dsc = fuse_bwd(d32, y, B, H, W, C, route_mask, scales)
-            dx, dq, dst = scan_bwd(x, states, heads, d, dyr, route_mask, q, record=rec, **kwc)
+            dx, dq, dst, dsc = scan_fuse_bwd(x, states, heads, d, y, scales, d32, route_mask, q,
+                                             record=rec, **kwc)
             grads = (dx.to(x.dtype), dst, dsc, None if dq is None else dq.to(q.dtype))
         if side is not None:
             cur.wait_stream(side)
