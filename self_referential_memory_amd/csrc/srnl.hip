@@ -3030,8 +3030,12 @@ srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W
         if (s != SRNL_OK)
             return s;
     }
-    hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, dout, y,
-                       scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
+    if (skip_dyr)
+        hipLaunchKernelGGL(fuse_bwd_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+                           dout, y, scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
+    else
+        hipLaunchKernelGGL(fuse_bwd_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+                           dout, y, scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
     s = launch_check("fuse_bwd_kernel");
     if (s != SRNL_OK)
         return s;
