@@ -2448,11 +2448,21 @@ BwdLayout bwd_layout(int B, int H, int W, int C, int heads, int d, unsigned mask
     return l;
 }
 
+// The fusion backward's part of the operator's one-call backward, run after
+// the windowed adjoint (its partial sums in one launch with the dx sum, then
+// the scales' gradient): dout [B][H][W][C], the route outputs y, the scales,
+// nfb partial-sum blocks of rb grid cells in part, dscales.
+struct FuseTail {
+    const float *dout, *y, *scales;
+    float *part, *dscales;
+    long long rb, nfb;
+};
+
 template <int D, typename InT>
 srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, int W, int C,
                             int heads, unsigned mask, const float *dy, float *ws,
                             const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out,
-                            const float *ysc)
+                            const float *ysc, const FuseTail *ft)
 {
     const int R = popcount4(mask);
     const int nchains = static_cast<int>(l.chains);
@@ -2526,7 +2536,16 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
     if (s != SRNL_OK)
         return s;
     const long long n = static_cast<long long>(B) * H * W * C;
-    hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, dxr, dx, R, n);
+    if (ft) {
+        const long long nsum = grid_for(n / 4, 256);
+        hipLaunchKernelGGL(bwd_tail_kernel, dim3(static_cast<unsigned>(ft->nfb + nsum)), dim3(256), 0, st,
+                           ft->dout, ft->y, ft->scales, ft->part, B, H, W, C, mask, ft->rb, ft->nfb,
+                           dxr, dx, R, n);
+        hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C * 64, 256)), dim3(256), 0, st,
+                           ft->part, ft->dscales, C, mask, static_cast<int>(ft->nfb));
+    } else {
+        hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, dxr, dx, R, n);
+    }
     if (p->q)
         hipLaunchKernelGGL(sum_slots_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, dqr, dq, R, n);
     const int sz = 3 * D * D + 2 * D;
@@ -2540,14 +2559,14 @@ template <typename InT>
 srnl_status dispatch_scan_bwd(int d, const void *x, const srnl_params *p, int B, int H, int W,
                               int C, int heads, unsigned mask, const float *dy, float *ws,
                               const BwdLayout &l, float *dx, float *dq, float *dstates, int nr_out,
-                              const float *ysc)
+                              const float *ysc, const FuseTail *ft)
 {
     switch (d) {
-    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
-    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
-    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
-    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
-    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc);
+    case 4: return launch_scan_bwd<4, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc, ft);
+    case 8: return launch_scan_bwd<8, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc, ft);
+    case 16: return launch_scan_bwd<16, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc, ft);
+    case 32: return launch_scan_bwd<32, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc, ft);
+    case 64: return launch_scan_bwd<64, InT>(x, p, B, H, W, C, heads, mask, dy, ws, l, dx, dq, dstates, nr_out, ysc, ft);
     }
     return fail(SRNL_ERR_ARG, "head dim must be 4, 8, 16, 32 or 64");
 }
@@ -2886,11 +2905,14 @@ namespace {
 // srnl_scan_bwd, with the state gradients written for route slots
 // 0 .. nr_out - 1 (4 for the 2-D operator, 1 for the 1-D one). With ysc
 // (the windowed d = 32 adjoint only), dy is the fused output's gradient
-// [B][H][W][C] and each route's dy is formed from it with the scales ysc.
+// [B][H][W][C] and each route's dy is formed from it with the scales ysc;
+// ft (with ysc): the fusion backward's partial sums and scales' gradient
+// run after the adjoint.
 srnl_status scan_bwd_impl(const void *x, int B, int H, int W, int C, int heads, int d,
                           unsigned route_mask, const srnl_params *p, const float *dy,
                           void *workspace, size_t workspace_bytes, float *dx, float *dq,
-                          float *dstates, int nr_out, const float *ysc = nullptr)
+                          float *dstates, int nr_out, const float *ysc = nullptr,
+                          const FuseTail *ft = nullptr)
 {
     long long n = 0;
     srnl_status s = check_scan_args(B, H, W, C, heads, d, route_mask, p, &n);
@@ -2925,9 +2947,9 @@ srnl_status scan_bwd_impl(const void *x, int B, int H, int W, int C, int heads, 
     float *ws = static_cast<float *>(workspace);
     if (p->in_dtype == SRNL_F32)
         return dispatch_scan_bwd<float>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
-                                        dstates, nr_out, ysc);
+                                        dstates, nr_out, ysc, ft);
     return dispatch_scan_bwd<uint16_t>(d, x, p, B, H, W, C, heads, route_mask, dy, ws, l, dx, dq,
-                                       dstates, nr_out, ysc);
+                                       dstates, nr_out, ysc, ft);
 }
 
 }   // namespace
@@ -2987,11 +3009,11 @@ namespace {
 // srnl_fuse_bwd with its partial sums in `workspace`, or (noalloc) in the
 // library's scratch array of this GPU
 // (dyr NULL with dyr_optional: only dscales; the route gradients are formed
-// by the windowed adjoint itself)
+// by the windowed adjoint itself. check_only: the checks, no launch.)
 srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W, int C,
                           unsigned route_mask, const float *scales, float *dyr, float *dscales,
                           void *workspace, size_t workspace_bytes, void *stream, bool noalloc,
-                          bool dyr_optional = false)
+                          bool dyr_optional = false, bool check_only = false)
 {
     long long n = 0;
     srnl_status s = check_grid(B, H, W, C, route_mask, &n);
@@ -3023,6 +3045,8 @@ srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W
     if (!aligned16(dout) || !aligned16(y) || !aligned16(scales) || (!skip_dyr && !aligned16(dyr)) ||
         !aligned16(dscales) || (!noalloc && !aligned16(workspace)))
         return fail(SRNL_ERR_PTR, "dout, y_routes, scales, dy_routes, dscales and workspace must be 16-byte aligned");
+    if (check_only)
+        return SRNL_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *part = static_cast<float *>(workspace);
     if (noalloc) {
@@ -3128,13 +3152,17 @@ srnl_status srnl_scan_fuse_bwd(const void *x, int B, int H, int W, int C, int he
         return fail(SRNL_ERR_WORKSPACE, "workspace smaller than srnl_scan_fuse_bwd_workspace_bytes");
     float *ws = static_cast<float *>(workspace);
     float *part = ws + o.scan, *dyr = o.direct ? nullptr : part + o.part;
+    // direct: the checks here, the fusion backward's kernels after the adjoint
     s = fuse_bwd_impl(dout, y_routes, B, H, W, C, route_mask, scales, dyr, dscales, part,
-                      static_cast<size_t>(o.part) * sizeof(float), p->stream, false, true);
+                      static_cast<size_t>(o.part) * sizeof(float), p->stream, false, true, o.direct);
     if (s != SRNL_OK)
         return s;
-    if (o.direct)
+    if (o.direct) {
+        const FuseTail ft{dout, y_routes, scales, part, dscales, kFuseBwdRows, fuse_bwd_blocks(B, H, W)};
         return scan_bwd_impl(x, B, H, W, C, heads, d, route_mask, p, dout, ws,
-                             static_cast<size_t>(o.scan) * sizeof(float), dx, dq, dstates, 4, scales);
+                             static_cast<size_t>(o.scan) * sizeof(float), dx, dq, dstates, 4, scales,
+                             &ft);
+    }
     return scan_bwd_impl(x, B, H, W, C, heads, d, route_mask, p, dyr, ws,
                          static_cast<size_t>(o.scan) * sizeof(float), dx, dq, dstates, 4);
 }
