@@ -2536,11 +2536,25 @@ srnl_status launch_scan_bwd(const void *x, const srnl_params *p, int B, int H, i
     if (s != SRNL_OK)
         return s;
     const long long n = static_cast<long long>(B) * H * W * C;
+    if (ft && !p->q && nr_out == 4) {
+        // the fusion partial sums, the dx sum and the state gradient in one
+        // launch, then the scales' gradient
+        const int sz = 3 * D * D + 2 * D;
+        const long long nsum = grid_for(n / 4, 256);
+        const long long nst = (4LL * heads * sz + 63) / 64;
+        hipLaunchKernelGGL(bwd_tail_kernel, dim3(static_cast<unsigned>(ft->nfb + nsum + nst)), dim3(256), 0,
+                           st, ft->dout, ft->y, ft->scales, ft->part, B, H, W, C, mask, ft->rb, ft->nfb,
+                           dxr, dx, R, n, nsum, dstp, dstates, heads, sz);
+        hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C * 64, 256)), dim3(256), 0, st,
+                           ft->part, ft->dscales, C, mask, static_cast<int>(ft->nfb));
+        return launch_check("scan_fuse_bwd tail");
+    }
     if (ft) {
+        // with separate queries: the dq sum too, as its own launch
         const long long nsum = grid_for(n / 4, 256);
         hipLaunchKernelGGL(bwd_tail_kernel, dim3(static_cast<unsigned>(ft->nfb + nsum)), dim3(256), 0, st,
                            ft->dout, ft->y, ft->scales, ft->part, B, H, W, C, mask, ft->rb, ft->nfb,
-                           dxr, dx, R, n);
+                           dxr, dx, R, n, nsum, nullptr, nullptr, heads, 0);
         hipLaunchKernelGGL(fuse_bwd_scales_kernel, dim3(grid_for(4LL * C * 64, 256)), dim3(256), 0, st,
                            ft->part, ft->dscales, C, mask, static_cast<int>(ft->nfb));
     } else {
