@@ -844,7 +844,6 @@ __global__ __launch_bounds__(NW * 64, (D == 32 && T == 16 && !SAVE && !HAS_Q) ? 
     constexpr int SEGS = D / VE;                       // 16-byte segments per token
     constexpr int NPF = (T * SEGS + NT - 1) / NT;      // prefetch registers per thread
     constexpr int RT = (3 * D / 16) * NTC;             // refresh tiles (matrix memories)
-    constexpr int RTW = (RT + NW - 1) / NW;            // refresh tiles per wave (at most)
 
     __shared__ __align__(16) float pool[Cfg::POOL];
     float *const Bs = pool + Cfg::O_BS;    // boundary rows M_c, M_k, M_v, m_eta, m_alpha
@@ -3022,12 +3021,12 @@ size_t srnl_fuse_bwd_workspace_bytes(int B, int H, int W, int C, unsigned route_
 namespace {
 // srnl_fuse_bwd with its partial sums in `workspace`, or (noalloc) in the
 // library's scratch array of this GPU
-// (dyr NULL with dyr_optional: only dscales; the route gradients are formed
-// by the windowed adjoint itself. check_only: the checks, no launch.)
+// (check_only: the checks alone, no launch, and dyr may be NULL, for the
+// one-call backward whose adjoint forms the route gradients itself)
 srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W, int C,
                           unsigned route_mask, const float *scales, float *dyr, float *dscales,
                           void *workspace, size_t workspace_bytes, void *stream, bool noalloc,
-                          bool dyr_optional = false, bool check_only = false)
+                          bool check_only = false)
 {
     long long n = 0;
     srnl_status s = check_grid(B, H, W, C, route_mask, &n);
@@ -3051,7 +3050,7 @@ srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W
     }
     if (nblk > 65535LL * 16)
         return fail(SRNL_ERR_ARG, "grid too large for srnl_fuse_bwd");
-    const bool skip_dyr = dyr_optional && dyr == nullptr;
+    const bool skip_dyr = check_only && dyr == nullptr;
     if (!is_device_ptr(dout) || !is_device_ptr(y) || !is_device_ptr(scales) ||
         (!skip_dyr && !is_device_ptr(dyr)) || !is_device_ptr(dscales) ||
         (!noalloc && !is_device_ptr(workspace)))
@@ -3068,12 +3067,8 @@ srnl_status fuse_bwd_impl(const float *dout, const float *y, int B, int H, int W
         if (s != SRNL_OK)
             return s;
     }
-    if (skip_dyr)
-        hipLaunchKernelGGL(fuse_bwd_kernel<false>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
-                           dout, y, scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
-    else
-        hipLaunchKernelGGL(fuse_bwd_kernel<true>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
-                           dout, y, scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
+    hipLaunchKernelGGL(fuse_bwd_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, dout, y,
+                       scales, dyr, part, B, H, W, C, route_mask, kFuseBwdRows);
     s = launch_check("fuse_bwd_kernel");
     if (s != SRNL_OK)
         return s;
@@ -3168,7 +3163,7 @@ srnl_status srnl_scan_fuse_bwd(const void *x, int B, int H, int W, int C, int he
     float *part = ws + o.scan, *dyr = o.direct ? nullptr : part + o.part;
     // direct: the checks here, the fusion backward's kernels after the adjoint
     s = fuse_bwd_impl(dout, y_routes, B, H, W, C, route_mask, scales, dyr, dscales, part,
-                      static_cast<size_t>(o.part) * sizeof(float), p->stream, false, true, o.direct);
+                      static_cast<size_t>(o.part) * sizeof(float), p->stream, false, o.direct);
     if (s != SRNL_OK)
         return s;
     if (o.direct) {
