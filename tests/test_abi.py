@@ -284,3 +284,42 @@ def test_fuse_bwd_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_wor
     assert L.srnl_fuse_bwd_noalloc(None, None, 700, 56, 56, 64, 15, None, None, None,
                                    None) == srnl.SRNL_ERR_WORKSPACE
     assert "scratch" in L.srnl_last_error().decode()
+
+
+def test_scan_fuse_bwd_workspace_and_argument_errors():
+    # the one-call backward: its workspace holds the scan backward's and the
+    # fusion backward's partial sums, plus the route gradients only where
+    # the windowed d = 32 adjoint (which forms them itself) does not run
+    L = srnl.lib()
+
+    def p(flags=0):
+        return srnl.Params(None, None, 0, 0.9, 1e-6, 0, 0, flags, None)
+
+    def sizes(B, H, W, heads, d, flags=0, mask=15):
+        C, R = heads * d, bin(mask).count("1")
+        pp = p(flags)
+        one = L.srnl_scan_fuse_bwd_workspace_bytes(B, H, W, C, heads, d, mask, ctypes.byref(pp))
+        scan = L.srnl_scan_bwd_workspace_bytes(B, H, W, C, heads, d, mask, ctypes.byref(pp))
+        fuse = L.srnl_fuse_bwd_workspace_bytes(B, H, W, C, mask)
+        return one, scan, fuse, 4 * R * B * H * W * C
+
+    one, scan, fuse, dyr = sizes(2, 9, 11, 2, 32)
+    assert scan + fuse <= one < scan + fuse + dyr
+    for d, heads, flags in ((16, 2, 0), (32, 2, srnl.FLAG_READ_BEFORE), (64, 1, 0)):
+        one, scan, fuse, dyr = sizes(2, 9, 11, heads, d, flags)
+        assert one >= scan + fuse + dyr
+    one, scan, fuse, dyr = sizes(1, 5, 7, 2, 32, mask=0b0101)
+    assert scan + fuse <= one < scan + fuse + dyr
+    pp = p()
+    assert L.srnl_scan_fuse_bwd_workspace_bytes(0, 4, 4, 64, 2, 32, 15, ctypes.byref(pp)) == 0
+    assert L.srnl_scan_fuse_bwd_workspace_bytes(1, 4, 4, 60, 2, 32, 15, ctypes.byref(pp)) == 0
+    assert L.srnl_scan_fuse_bwd_workspace_bytes(1, 4, 4, 64, 2, 32, 15, None) == 0
+    # invalid arguments are reported before any device work
+    args = (None, None, None, None, 0, None, None, None, None)
+    assert L.srnl_scan_fuse_bwd(None, 1, 4, 4, 60, 2, 32, 15, ctypes.byref(pp), *args) == srnl.SRNL_ERR_ARG
+    assert L.srnl_scan_fuse_bwd(None, 1, 4, 4, 64, 2, 12, 15, ctypes.byref(pp), *args) == srnl.SRNL_ERR_ARG
+    assert L.srnl_scan_fuse_bwd(None, 1, 4, 4, 64, 2, 32, 15, None, *args) == srnl.SRNL_ERR_PTR
+    assert L.srnl_scan_fuse_bwd(None, 0, 4, 4, 64, 2, 32, 15, ctypes.byref(pp), *args) == srnl.SRNL_OK
+    # too small a workspace
+    assert L.srnl_scan_fuse_bwd(None, 1, 4, 4, 64, 2, 32, 15, ctypes.byref(pp), None, None, None,
+                                None, 16, None, None, None, None) == srnl.SRNL_ERR_WORKSPACE
